@@ -1,0 +1,248 @@
+"""Pins that tie the CPU oracle to facts fixed outside itself.
+
+Each pin returns None on success and raises AssertionError otherwise.  They are
+collected by tests/test_oracle.py and re-run against deliberately broken builds
+of the oracle by the mutation test (every broken build must fail at least one).
+
+Sources of truth used here, none of which call into the oracle's code:
+  * brute force on tiny inputs: exact sums (math.fsum) and the plain softmax
+    definition without max subtraction, and mpmath at 50 digits;
+  * library routines: scipy.special.softmax / logsumexp on a numpy score matrix;
+  * closed forms: Q = 0 gives the column mean of V and LSE = ln N, constant V
+    gives that constant, two keys give a logistic weighting, identical keys give
+    the plain mean;
+  * invariants: rows of P sum to one, joint K/V row permutation, key shift;
+  * the online-softmax recurrences agree with the full-row max and sum-exp after
+    every block, and reach the three-step O and LSE.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle
+from synth.inputs import make_qkv, quantize, to_float32
+
+
+def _f64(bits, dtype):
+    return to_float32(bits, dtype).astype(np.float64)
+
+
+# ---------------------------------------------------------------- brute force
+def _brute_fsum(qf, kf, vf, scale):
+    """Exact-sum brute force of one head: softmax by its definition exp(s)/sum exp(s)."""
+    N, d = qf.shape
+    O = np.empty((N, d))
+    L = np.empty(N)
+    for i in range(N):
+        s = [scale * math.fsum(float(qf[i, t]) * float(kf[j, t]) for t in range(d))
+             for j in range(N)]
+        e = [math.exp(x) for x in s]
+        z = math.fsum(e)
+        for t in range(d):
+            O[i, t] = math.fsum(e[j] * float(vf[j, t]) for j in range(N)) / z
+        L[i] = math.log(z)
+    return O, L
+
+
+def _brute_mp(qf, kf, vf, scale, dps=50):
+    import mpmath
+
+    with mpmath.workdps(dps):
+        N, d = qf.shape
+        O = np.empty((N, d))
+        L = np.empty(N)
+        sc = mpmath.mpf(scale)
+        for i in range(N):
+            s = [sc * mpmath.fsum(mpmath.mpf(float(qf[i, t])) * mpmath.mpf(float(kf[j, t]))
+                                  for t in range(d)) for j in range(N)]
+            e = [mpmath.exp(x) for x in s]
+            z = mpmath.fsum(e)
+            for t in range(d):
+                O[i, t] = float(mpmath.fsum(e[j] * mpmath.mpf(float(vf[j, t]))
+                                            for j in range(N)) / z)
+            L[i] = float(mpmath.log(z))
+    return O, L
+
+
+def pin_brute_force(cases=None):
+    """Oracle O/LSE equal brute force at N <= 64 (fsum) and on tiny cases (mpmath)."""
+    if cases is None:
+        cases = [("f32", 1, 2, 64, 16, 0.25, "fsum"), ("f16", 1, 1, 48, 64, 0.125, "fsum"),
+                 ("bf16", 2, 1, 33, 8, 0.35, "fsum"), ("f16", 1, 1, 7, 5, 0.6, "mp"),
+                 ("bf16", 1, 1, 5, 3, 1.7, "mp"), ("f32", 1, 1, 1, 4, 0.5, "mp")]
+    for dtype, B, H, N, d, scale, how in cases:
+        x = make_qkv(B, H, N, d, dtype, seed=100 + N + d, mult=1.5)
+        o, lse = oracle.attention(x["q"], x["k"], x["v"], dtype, scale)
+        qf, kf, vf = (_f64(x[n], dtype) for n in "qkv")
+        for b in range(B):
+            for h in range(H):
+                f = _brute_fsum if how == "fsum" else _brute_mp
+                Ob, Lb = f(qf[b, h], kf[b, h], vf[b, h], scale)
+                vmax = max(1.0, np.abs(vf[b, h]).max())
+                err_o = np.abs(o[b, h] - Ob).max() / vmax
+                err_l = np.abs(lse[b, h] - Lb).max() / max(1.0, np.abs(Lb).max())
+                assert err_o <= 1e-12, f"brute force O mismatch {err_o:.3e} ({dtype},{N},{d})"
+                assert err_l <= 1e-12, f"brute force LSE mismatch {err_l:.3e} ({dtype},{N},{d})"
+
+
+# ----------------------------------------------------------- library routines
+def pin_scipy_softmax_logsumexp():
+    """S equals scale*QK^T (numpy matmul), P equals scipy softmax(S), LSE equals logsumexp(S)."""
+    from scipy.special import logsumexp, softmax
+
+    for dtype, N, d, scale in (("f16", 96, 64, 0.125), ("bf16", 40, 128, 0.0884), ("f32", 50, 24, 0.3)):
+        x = make_qkv(1, 1, N, d, dtype, seed=7 * N + d, mult=2.0)
+        s, p, o, lse = oracle.head_steps(x["q"], x["k"], x["v"], dtype, scale)
+        qf, kf, vf = (_f64(x[n], dtype)[0, 0] for n in "qkv")
+        s_ref = scale * (qf @ kf.T)
+        assert np.abs(s - s_ref).max() <= 1e-12 * max(1.0, np.abs(s_ref).max()), "S != scale QK^T"
+        assert np.abs(p - softmax(s_ref, axis=1)).max() <= 1e-12, "P != scipy softmax"
+        assert np.abs(lse - logsumexp(s_ref, axis=1)).max() <= 1e-12 * np.abs(lse).max(), \
+            "LSE != scipy logsumexp"
+        assert np.abs(o - softmax(s_ref, axis=1) @ vf).max() <= 1e-12 * np.abs(vf).max(), \
+            "O != softmax(S) V"
+        # the sampled-row entry point agrees with the head entry point
+        o2, l2 = oracle.attention(x["q"], x["k"], x["v"], dtype, scale)
+        assert np.abs(o2[0, 0] - o).max() <= 1e-13 and np.abs(l2[0, 0] - lse).max() <= 1e-13
+
+
+# ----------------------------------------------------------------- closed forms
+def pin_rows_sum_to_one():
+    x = make_qkv(1, 1, 77, 32, "bf16", seed=5, mult=3.0)
+    s, p, o, lse = oracle.head_steps(x["q"], x["k"], x["v"], "bf16", 0.2)
+    assert np.all(p >= 0.0)
+    assert np.abs(p.sum(axis=1) - 1.0).max() <= 1e-13 * 77, "rows of P do not sum to 1"
+
+
+def pin_zero_query():
+    """Q = 0: every score is 0, so O = column mean of V (over the N keys) and LSE = ln N."""
+    for dtype in ("f32", "f16", "bf16"):
+        B, H, N, d = 2, 3, 37, 16
+        x = make_qkv(B, H, N, d, dtype, seed=3)
+        zero = quantize(np.zeros((B, H, N, d), np.float32), dtype)
+        o, lse = oracle.attention(zero, x["k"], x["v"], dtype, 0.25)
+        vf = _f64(x["v"], dtype)
+        mean = vf.mean(axis=2, keepdims=True)
+        assert np.abs(o - mean).max() <= 1e-12, "Q=0 does not give the column mean of V"
+        assert np.abs(lse - math.log(N)).max() <= 1e-12, "Q=0 does not give LSE = ln N"
+        # K = 0 is the same closed form
+        o, lse = oracle.attention(x["q"], zero, x["v"], dtype, 0.25)
+        assert np.abs(o - mean).max() <= 1e-12 and np.abs(lse - math.log(N)).max() <= 1e-12
+
+
+def pin_constant_v():
+    for dtype, c in (("f32", -2.75), ("f16", 3.5), ("bf16", 0.15625)):
+        B, H, N, d = 1, 2, 29, 8
+        x = make_qkv(B, H, N, d, dtype, seed=9, mult=4.0)
+        vc = quantize(np.full((B, H, N, d), c, np.float32), dtype)
+        o, _ = oracle.attention(x["q"], x["k"], vc, dtype, 0.5)
+        assert np.abs(o - c).max() <= 1e-12 * abs(c) * 4, "constant V not returned"
+
+
+def pin_two_keys():
+    """N = 2, d = 1: q = 1, keys (0, a) give weights (1, e^{sa}) / (1 + e^{sa}).
+    Query 2 has q = -1, so its weights are (1, e^{-sa}) / (1 + e^{-sa})."""
+    a, v0, v1, scale = 1.5, 2.0, -3.0, 0.75
+    q = np.array([1.0, -1.0], np.float32).reshape(1, 1, 2, 1)
+    k = np.array([0.0, a], np.float32).reshape(1, 1, 2, 1)
+    v = np.array([v0, v1], np.float32).reshape(1, 1, 2, 1)
+    o, lse = oracle.attention(q, k, v, "f32", scale)
+    for i, sgn in enumerate((1.0, -1.0)):
+        w1 = 1.0 / (1.0 + math.exp(-sgn * scale * a))  # logistic weight of key 1
+        assert abs(o[0, 0, i, 0] - ((1 - w1) * v0 + w1 * v1)) <= 1e-15 * 4
+        assert abs(lse[0, 0, i] - math.log(1.0 + math.exp(sgn * scale * a))) <= 1e-15 * 4
+
+
+def pin_identical_keys_large_logits():
+    """All keys equal and logits huge (s ~ 2.6e3): the max subtraction keeps it finite;
+    O is the plain mean of V and LSE = s + ln N."""
+    N, d = 24, 64
+    q = np.full((1, 1, N, d), 6.5, np.float32)
+    k = np.full((1, 1, N, d), 6.25, np.float32)
+    v = make_qkv(1, 1, N, d, "f32", seed=1)["v"]
+    o, lse = oracle.attention(q, k, v, "f32", 1.0)
+    s = 6.5 * 6.25 * d
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.abs(o[0, 0] - v[0, 0].astype(np.float64).mean(axis=0)).max() <= 1e-12
+    assert np.abs(lse[0, 0] - (s + math.log(N))).max() <= 1e-12 * s
+
+
+def pin_large_spread_logits():
+    """Scores 1000, 0, -1000 (d = 1, q = 1): without subtracting the row max, exp would
+    overflow.  The first key takes all the weight in double precision, so O = v_0
+    exactly and LSE = 1000 (e^-1000 is below double's range)."""
+    q = np.ones((1, 1, 3, 1), np.float32)
+    k = np.array([1000.0, 0.0, -1000.0], np.float32).reshape(1, 1, 3, 1)
+    v = np.array([1.25, -7.0, 3.0], np.float32).reshape(1, 1, 3, 1)
+    o, lse = oracle.attention(q, k, v, "f32", 1.0)
+    assert np.all(o[0, 0, :, 0] == 1.25), f"large-spread O wrong: {o.ravel()}"
+    assert np.all(lse[0, 0] == 1000.0), f"large-spread LSE wrong: {lse.ravel()}"
+
+
+# ----------------------------------------------------------------- invariants
+def pin_permutation_invariance():
+    x = make_qkv(1, 2, 45, 16, "f16", seed=21)
+    o, lse = oracle.attention(x["q"], x["k"], x["v"], "f16", 0.3)
+    perm = np.random.Generator(np.random.PCG64(4)).permutation(45)
+    o2, lse2 = oracle.attention(x["q"], x["k"][:, :, perm], x["v"][:, :, perm], "f16", 0.3)
+    assert np.abs(o - o2).max() <= 1e-13 and np.abs(lse - lse2).max() <= 1e-13
+    # a K-only permutation must change the result (guards against ignoring the pairing)
+    o3, _ = oracle.attention(x["q"], x["k"][:, :, perm], x["v"], "f16", 0.3)
+    assert np.abs(o - o3).max() > 1e-3
+
+
+def pin_key_shift():
+    """K += 1 u^T leaves O unchanged and moves LSE_i by scale * <q_i, u>.
+    Integer-valued inputs keep every value exact in float32."""
+    rng = np.random.Generator(np.random.PCG64(8))
+    N, d, scale = 31, 12, 0.375
+    q = rng.integers(-3, 4, (1, 1, N, d)).astype(np.float32)
+    k = rng.integers(-3, 4, (1, 1, N, d)).astype(np.float32)
+    v = rng.integers(-5, 6, (1, 1, N, d)).astype(np.float32)
+    u = rng.integers(-2, 3, d).astype(np.float32)
+    o, lse = oracle.attention(q, k, v, "f32", scale)
+    o2, lse2 = oracle.attention(q, k + u, v, "f32", scale)
+    shift = scale * (q[0, 0].astype(np.float64) @ u.astype(np.float64))
+    assert np.abs(o - o2).max() <= 1e-12
+    assert np.abs((lse2 - lse)[0, 0] - shift).max() <= 1e-12 * max(1.0, np.abs(lse).max())
+
+
+# ------------------------------------------------------------ online softmax
+def pin_online_equals_three_step():
+    """Blockwise recurrences: after block j, m is the max of the scores seen so far
+    (exactly) and l is their sum of exp(s - m); the end result is the three-step O and LSE."""
+    for dtype, N, d in (("f16", 64, 16), ("bf16", 50, 8), ("f32", 17, 4)):
+        x = make_qkv(1, 1, N, d, dtype, seed=N, mult=2.5)
+        scale = 1.0 / math.sqrt(d)
+        s, p, o3, l3 = oracle.head_steps(x["q"], x["k"], x["v"], dtype, scale)
+        for block in (1, 3, 16, 64, N):
+            o, lse, mt, lt = oracle.online_head(x["q"], x["k"], x["v"], dtype, scale, block)
+            nb = mt.shape[1]
+            for jb in range(nb):
+                hi = min(N, (jb + 1) * block)
+                pref = s[:, :hi]
+                mref = pref.max(axis=1)
+                assert np.array_equal(mt[:, jb], mref), f"online m != prefix max (block {block})"
+                lref = np.exp(pref - mref[:, None]).sum(axis=1)
+                assert np.abs(lt[:, jb] - lref).max() <= 1e-12 * lref.max(), \
+                    f"online l != prefix sum-exp (block {block})"
+            assert np.abs(o - o3).max() <= 1e-12 * max(1.0, np.abs(o3).max()), \
+                f"online O != three-step O (block {block})"
+            assert np.abs(lse - l3).max() <= 1e-12 * np.abs(l3).max()
+
+
+ALL_PINS = [
+    pin_brute_force,
+    pin_scipy_softmax_logsumexp,
+    pin_rows_sum_to_one,
+    pin_zero_query,
+    pin_constant_v,
+    pin_two_keys,
+    pin_identical_keys_large_logits,
+    pin_large_spread_logits,
+    pin_permutation_invariance,
+    pin_key_shift,
+    pin_online_equals_three_step,
+]
