@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention forward (fa_fwd) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--path fused|naive]
+
+One step is one fa_fwd call over the whole workload (all B*H heads, all N query
+rows).  Inputs are seeded synthetic tensors already resident in device memory when
+the timed region starts.  Prints ONE JSON line with:
+  value      TFLOP/s, counting 4*B*H*N^2*d flops per step
+  roofline   the fused kernel against the dense bf16/fp16 matrix-core peak, timed with
+             HIP events around every launch on the launch stream; `traffic` comes from
+             the committed rocprofv3 counter summary when it was taken on this exact
+             kernel source, else null
+  cpu_baseline  the CPU fp64 oracle timed on this host on a bounded sample of the same
+             workload's query rows (a reported baseline, not the target)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from synth.configs import WORKLOADS  # noqa: E402
+
+METRIC = "fwd attention TFLOP/s & % of bf16 MFMA peak, B8 H32 N4096 d128"
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # MI355X dense matrix-core peaks
+KERNEL_SOURCES = ("exact_attention_90_amd/csrc/fa_fused.hip",
+                  "exact_attention_90_amd/csrc/fa_device.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str, path: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    summary is missing or was taken on different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    src = kernel_source_hash()
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"\s*traffic-json:\s*(\{.*\})\s*$", line)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("workload") == workload and rec.get("path") == path and rec.get("kernel_src") == src:
+            return rec
+    return None
+
+
+def cpu_baseline(x, w, o_gpu, lse_gpu, target_s: float):
+    """Time the oracle on evenly spaced query rows (about target_s seconds) and check
+    those rows of the GPU output against it."""
+    import numpy as np
+
+    import oracle
+
+    total = w.rows
+    flops_row = 4.0 * w.N * w.d
+    scale32 = float(np.float32(w.scale))
+    # calibrate on a strided sample of the same shape as the timed one (the oracle
+    # widens each head's K and V once, so scattered rows cost more per row)
+    cstride = max(1, total // 2048)
+    calib = np.arange(0, total, cstride, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.attention(x["q"], x["k"], x["v"], w.dtype, scale32, rows=calib)
+    per_row = (time.perf_counter() - t0) / len(calib)
+    n = int(min(total, max(64, target_s / max(per_row, 1e-9))))
+    stride = max(1, total // n)
+    rows = np.arange(0, total, stride, dtype=np.int64)[:n]
+    t0 = time.perf_counter()
+    o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], w.dtype, scale32, rows=rows)
+    dt = time.perf_counter() - t0
+    import torch
+
+    idx = torch.from_numpy(rows).to(o_gpu.device)
+    og = o_gpu.reshape(-1, w.d).index_select(0, idx).cpu().numpy().astype(np.float64)
+    lg = lse_gpu.reshape(-1).index_select(0, idx).cpu().numpy().astype(np.float64)
+    parity = {
+        "rows": int(len(rows)),
+        "max_abs": float(np.abs(og - o_ref).max()),
+        "cosine": float((og.ravel() @ o_ref.ravel()) /
+                        (np.linalg.norm(og) * np.linalg.norm(o_ref))),
+        "lse_rel": float((np.abs(lg - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)).max()),
+    }
+    base = {
+        "value": flops_row * len(rows) / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(oracle.num_threads()),
+        "kind": "oracle",
+        "sample": (f"{len(rows)} of {total} query rows of {w.name} ({w.short()}), every "
+                   f"{stride}-th row, each against all N={w.N} keys; fp64 C oracle, "
+                   f"{dt:.1f} s"),
+    }
+    return base, parity
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--path", default="fused", choices=["fused", "naive"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); sharding across GPUs is described, not run.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import exact_attention_90_amd as fa
+    from synth.inputs import make_qkv, to_torch
+
+    w = WORKLOADS[args.workload]
+    scale32 = float(np.float32(w.scale))
+    print(f"[bench] generating {w.name}: {w.short()}", file=sys.stderr, flush=True)
+    x = make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.mult)
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch(x[n], w.dtype).to(dev) for n in ("q", "k", "v"))
+    o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    ws = None
+    if args.path == "naive":
+        nb = fa.naive_workspace_bytes(w.B, w.H, w.N, q.dtype)
+        ws = (torch.empty(nb, dtype=torch.uint8, device=dev),
+              torch.empty(nb, dtype=torch.uint8, device=dev))
+
+    def step():
+        if args.path == "fused":
+            fa.fwd(q, k, v, scale32, out=o, lse=lse)
+        else:
+            fa.naive_fwd(q, k, v, scale32, out=o, lse=lse, workspace=ws)
+
+    stream = torch.cuda.current_stream(dev)  # the stream every launch goes to
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    # timed region: events around every launch, on the launch stream
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize(dev)
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    ms_total = evs[0].elapsed_time(evs[-1])
+    ms_step = ms_total / args.steps
+    flops = float(w.flops)
+    value = flops / (ms_step * 1e-3) / 1e12
+    avg_launch_ms = sum(per) / len(per)
+    peak = PEAK_TFLOPS[w.dtype]
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+
+    traffic = None
+    rec = committed_traffic(w.name, args.path)
+    if rec is not None:
+        traffic = rec.get("bytes_per_launch")
+
+    line = {
+        "metric": METRIC if w.name == "c3" and args.path == "fused" else
+        f"fwd attention TFLOP/s ({args.path}), {w.short()}",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: non-causal attention forward, {w.short()}, "
+                        f"scale 1/sqrt({w.d}), O fp32 + LSE",
+            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "path": args.path,
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel": "fa_fwd16_kernel" if w.dtype != "f32" else "fa_fwd32_kernel",
+            "avg_launch_ms": round(avg_launch_ms, 5),
+            "min_launch_ms": round(min(per), 5),
+            "kernel_src": kernel_source_hash(),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
+        base, parity = cpu_baseline(x, w, o, lse, args.cpu_seconds)
+        line["cpu_baseline"] = base
+        line["parity_sample"] = parity
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,107 @@
+"""Python binding of libfa.so (argument marshalling only).
+
+PyTorch supplies device memory and the stream; every step of the computation runs
+in the library's HIP kernels.  The function names follow the C boundary:
+
+    fwd(q, k, v, scale=None)        -> (o, lse)   fused FlashAttention forward
+    naive_fwd(q, k, v, scale=None)  -> (o, lse)   materialised S/P contrast path
+
+q, k, v: contiguous [B, H, N, d] device tensors of one dtype (float32, float16 or
+bfloat16), d in {64, 128}.  o is float32 [B, H, N, d]; lse is float32 [B, H, N]
+(natural log).  scale defaults to 1/sqrt(d).
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+
+_CODES = {torch.float32: _lib.FA_F32, torch.float16: _lib.FA_F16, torch.bfloat16: _lib.FA_BF16}
+
+
+def _check_inputs(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor (got {t.device})")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _CODES:
+        raise TypeError("q, k, v must share one dtype among float32, float16, bfloat16")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+
+
+def _outputs(q, out, lse):
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor shaped like q")
+    if lse.dtype != torch.float32 or lse.shape != q.shape[:3] or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    return out, lse
+
+
+def _stream(q, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    return ctypes_stream(stream)
+
+
+def ctypes_stream(stream) -> int:
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream or 0)
+
+
+def fwd(q, k, v, scale: float | None = None, out=None, lse=None, stream=None):
+    """Fused attention forward: returns (o, lse); enqueued on `stream` (default: current)."""
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q, out, lse)
+    lib = _lib.load()
+    rc = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
+                    H, N, d, scale, _CODES[q.dtype], _stream(q, stream))
+    _lib.check(rc, "fa_fwd")
+    return out, lse
+
+
+def naive_workspace_bytes(B: int, H: int, N: int, dtype) -> int:
+    code = _CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.load().fa_naive_workspace_bytes(B, H, N, code))
+
+
+def naive_fwd(q, k, v, scale: float | None = None, out=None, lse=None, workspace=None,
+              stream=None):
+    """Materialised three-kernel path: returns (o, lse).
+
+    workspace: optional pair of uint8 device tensors (S, P), each at least
+    naive_workspace_bytes(B, H, N, dtype) bytes; allocated when omitted."""
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q, out, lse)
+    nbytes = naive_workspace_bytes(B, H, N, q.dtype)
+    if workspace is None:
+        workspace = (torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device),
+                     torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device))
+    s_ws, p_ws = workspace
+    if s_ws.numel() * s_ws.element_size() < nbytes or p_ws.numel() * p_ws.element_size() < nbytes:
+        raise ValueError("naive workspace too small")
+    lib = _lib.load()
+    rc = lib.fa_naive_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), s_ws.data_ptr(), p_ws.data_ptr(), B, H, N, d, scale,
+                          _CODES[q.dtype], _stream(q, stream))
+    _lib.check(rc, "fa_naive_fwd")
+    return out, lse
+
+
+def version() -> str:
+    return _lib.load().fa_version().decode()

@@ -1,0 +1,133 @@
+// C boundary of libfa.so: argument checks, then one launch sequence on the caller's
+// stream.  The contract of every entry point is documented in include/fa.h.
+#include "fa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Checks shared by both paths.  Sets *empty when there is nothing to compute.
+int check_args(const void *q, const void *k, const void *v, const float *o, const float *lse,
+               int B, int H, int N, int d, float scale, int dtype, bool *empty) {
+  *empty = false;
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA_OK;
+  }
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_ALIGN;
+  // index limits: B*H heads must fit an int, the grid must stay within kMaxGrid
+  const int64_t heads = int64_t(B) * H;
+  if (heads > std::numeric_limits<int>::max()) return FA_ERR_SHAPE;
+  const int64_t qtiles = (int64_t(N) + fa::kFusedBM - 1) / fa::kFusedBM;
+  if (heads * qtiles > fa::kMaxGrid) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  g_last_hip_error = int(e);
+  return FA_ERR_HIP;
+}
+
+int device_ready() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  return FA_OK;
+}
+
+fa::Problem make_problem(const void *q, const void *k, const void *v, float *o, float *lse,
+                         int B, int H, int N, int d, float scale, int dtype) {
+  fa::Problem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.dtype = dtype;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int N,
+           int d, float scale, int dtype, void *stream) {
+  bool empty = false;
+  int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
+  if (rc != FA_OK || empty) return rc;
+  rc = device_ready();
+  if (rc != FA_OK) return rc;
+  return hip_status(fa::launch_fused(make_problem(q, k, v, o, lse, B, H, N, d, scale, dtype),
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype) {
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return 0;
+  if (B < 0 || H < 0 || N < 0) return 0;
+  const unsigned __int128 n = (unsigned __int128)(uint64_t)B * (uint64_t)H * (uint64_t)N *
+                              (uint64_t)N * (uint64_t)elem_bytes(dtype);
+  const unsigned __int128 rounded = (n + 255) / 256 * 256;
+  if (rounded > (unsigned __int128)std::numeric_limits<size_t>::max())
+    return std::numeric_limits<size_t>::max();
+  return (size_t)rounded;
+}
+
+int fa_naive_fwd(const void *q, const void *k, const void *v, float *o, float *lse, void *s_ws,
+                 void *p_ws, int B, int H, int N, int d, float scale, int dtype, void *stream) {
+  bool empty = false;
+  int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
+  if (rc != FA_OK || empty) return rc;
+  if (!s_ws || !p_ws || !aligned(s_ws, 16) || !aligned(p_ws, 16)) return FA_ERR_WORKSPACE;
+  if (fa_naive_workspace_bytes(B, H, N, dtype) == std::numeric_limits<size_t>::max())
+    return FA_ERR_SHAPE;
+  rc = device_ready();
+  if (rc != FA_OK) return rc;
+  return hip_status(fa::launch_naive(make_problem(q, k, v, o, lse, B, H, N, d, scale, dtype), s_ws,
+                                     p_ws, static_cast<hipStream_t>(stream)));
+}
+
+const char *fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid or too large B, H or N";
+    case FA_ERR_HEADDIM: return "head dimension must be 64 or 128";
+    case FA_ERR_DTYPE: return "unknown dtype";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_WORKSPACE: return "naive-path workspace NULL or misaligned";
+    case FA_ERR_HIP: return "HIP error (no device or launch failure)";
+    default: return "unknown status";
+  }
+}
+
+const char *fa_version(void) { return "exact_attention_90_amd 0.1.0 gfx950"; }
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

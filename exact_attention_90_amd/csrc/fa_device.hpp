@@ -1,0 +1,140 @@
+// Device-side building blocks for the gfx950 attention kernels: vector types,
+// matrix-core wrappers, LDS address swizzles and lane exchanges.
+//
+// Register layouts used throughout (checked against exact integer products on
+// gfx950; "lane" is the lane id 0..63, "h" = lane / 32):
+//   v_mfma_f32_32x32x16_{bf16,f16}  A[32 x 16]: lane holds A[lane % 32][8h .. 8h+7]
+//                                   B[16 x 32]: lane holds B[8h .. 8h+7][lane % 32]
+//                                   C[32 x 32]: register r of lane holds
+//                                     C[8*(r/4) + 4h + r%4][lane % 32]
+//   v_mfma_f32_32x32x2_f32          A: lane holds A[lane % 32][h], B: B[h][lane % 32],
+//                                   C as above.
+//   ds_read_b64_tr_b16              within each group of 16 lanes, lane i receives, for
+//                                   s = 0..3, element (i % 4) of the four 16-bit values
+//                                   addressed by lane 4s + i/4 of its group.
+//   v_permlane32_swap               exchanges a register between lane l and lane l ^ 32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- matrix cores ---------------------------------------------------------------
+__device__ __forceinline__ f32x16 mma_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mma_f16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <bool BF16>
+__device__ __forceinline__ f32x16 mma16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (BF16)
+    return mma_bf16(a, b, c);
+  else
+    return mma_f16(a, b, c);
+}
+__device__ __forceinline__ f32x16 mma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// ---- lane exchange --------------------------------------------------------------
+// v_permlane32_swap(a, b) swaps the upper 32 lanes of a with the lower 32 lanes of b.
+// With a = b = x the two results hold, on every lane l, x[min(l, l^32)] and
+// x[max(l, l^32)]: the lane's own value and its partner's, in the same order on
+// both lanes of a pair, so the combined value below is bitwise equal on both.
+__device__ __forceinline__ void pair_values(float x, float &lo, float &hi) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  lo = __builtin_bit_cast(float, (uint32_t)p[0]);
+  hi = __builtin_bit_cast(float, (uint32_t)p[1]);
+}
+__device__ __forceinline__ float pair_max(float x) {
+  float a, b;
+  pair_values(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  float a, b;
+  pair_values(x, a, b);
+  return a + b;
+}
+
+// ---- fast math ---------------------------------------------------------------------
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// ---- conversions -----------------------------------------------------------------
+// two fp32 -> packed binary16, round to nearest even
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// two packed bfloat16 -> two packed binary16 (exact for normal binary16 range)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  float lo = __builtin_bit_cast(float, w << 16);
+  float hi = __builtin_bit_cast(float, w & 0xffff0000u);
+  return pack_f16(lo, hi);
+}
+
+// ---- LDS swizzles (units: 16-byte chunks; cpr = chunks per row) -------------------
+// Row-operand tiles (Q, K) are read 16 bytes per lane with 16 lanes on 16
+// consecutive rows at the same logical chunk: spread those 16 rows over all banks.
+template <int CPR>
+__device__ __forceinline__ int swz_row(int r, int ch) {
+  if constexpr (CPR == 8)
+    return ch ^ ((r >> 1) & 7);
+  else
+    return ch ^ (r & 15);
+}
+// V tiles are read with the transposing load: 8 consecutive rows, each reading one
+// 64-byte block (4 chunks).  Rotate the 64-byte blocks so 4 consecutive rows cover
+// all 256 bytes of the bank space.
+template <int CPR>
+__device__ __forceinline__ int swz_v(int r, int ch) {
+  if constexpr (CPR == 8)
+    return ch ^ (((r >> 1) & 1) << 2);
+  else
+    return ch ^ ((r & 3) << 2);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const char *base, int byte_off) {
+  return *reinterpret_cast<const u32x4 *>(base + byte_off);
+}
+__device__ __forceinline__ void lds_write16(char *base, int byte_off, u32x4 v) {
+  *reinterpret_cast<u32x4 *>(base + byte_off) = v;
+}
+__device__ __forceinline__ u32x2 lds_read_tr(const char *base, int byte_off) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + byte_off));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// ---- workgroup order ----------------------------------------------------------------
+// Workgroups are handed to the 8 XCDs round-robin (id % 8).  Renumber them so that
+// consecutive logical ids - the Q tiles of one head, which read the same K/V -
+// run on one XCD and share its L2.  Bijective for any grid size G.
+__device__ __forceinline__ int xcd_remap(int w, int G) {
+  int per = G >> 3, rem = G & 7;
+  int x = w & 7, idx = w >> 3;
+  return x * per + (x < rem ? x : rem) + idx;
+}
+
+}  // namespace fa

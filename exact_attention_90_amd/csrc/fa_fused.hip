@@ -1,0 +1,437 @@
+// Fused attention forward for gfx950 (FlashAttention forward pass).
+//
+// Algorithm: MUSA SDK guide "FlashAttention optimization", FlashAttention formula
+// steps 1-4 / a-f, with the FlashAttention-2 split of the grid over Q blocks
+// (same guide, "FlashAttention-2 improvement") and the Q-resident, K/V-streaming
+// loop order of the pwwt.cn CK/MI50 notes (section 2.2).  Per workgroup:
+//
+//   prologue  Q tile [128 x d] -> LDS with coalesced 16-byte loads -> registers
+//   loop      K_j, V_j tiles stream through two LDS stages; while tile j is used,
+//             tile j+1 is already in flight from global memory
+//             S^T = K_j Q^T on the matrix cores (fp32 accumulate)
+//             online softmax in registers: m_new = max(m, rowmax S),
+//             alpha = 2^(c m - c m_new), P = 2^(c S - c m_new), l = alpha l + rowsum P,
+//             with c = scale * log2(e) folded into one multiply-add per score
+//             O = alpha O (rescaled BEFORE the new block is added), then
+//             O^T += V_j^T P^T on the matrix cores
+//   epilogue  O / l and LSE = m*scale + ln l to global memory
+//
+// Layout of the work on the chip: 4 waves x 32 query rows.  Each wave computes S^T so
+// that every lane owns ONE query row and 16 (of 32) keys per 32x32 block: the row
+// max and row sum are in-lane reductions plus one exchange with lane ^ 32, and the
+// rescale factor alpha is a per-lane scalar.  The P registers feed the P V product
+// directly; V stays row-major in LDS and its operand is fetched with the
+// transposing LDS load in the same key order the P registers hold.
+#include "fa_device.hpp"
+#include "fa_internal.h"
+
+namespace fa {
+
+// ------------------------------------------------------------------------------------
+// Online softmax over one key tile (shared by the 16-bit and fp32 variants).
+//   s[SB]   scores of the tile (S^T blocks of 32 keys), replaced by P in place
+//   o[OB]   output accumulator, rescaled by alpha
+//   mc, l   running max (pre-multiplied by c) and this lane's partial row sum
+//   nvalid  number of valid keys in the tile (keys >= nvalid are masked to -inf)
+// ------------------------------------------------------------------------------------
+template <int SB, int OB, bool MASK>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[SB], f32x16 (&o)[OB], float &mc, float &l,
+                                             float c, int nvalid, int h) {
+  if constexpr (MASK) {
+#pragma unroll
+    for (int t = 0; t < SB; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key >= nvalid) s[t][r] = -INFINITY;
+      }
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int t = 0; t < SB; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+  mx = pair_max(mx);                       // full row max over the tile's keys
+  const float mc_new = fmaxf(mc, mx * c);  // running max in base-2 units
+  // a row that has seen only masked keys keeps alpha = 0 and P = 0 (no inf - inf)
+  const float alpha = (mc == -INFINITY) ? 0.f : ex2(mc - mc_new);
+  const float sub = (mc_new == -INFINITY) ? 0.f : mc_new;
+  float rs = 0.f;
+#pragma unroll
+  for (int t = 0; t < SB; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = ex2(fmaf(s[t][r], c, -sub));
+      s[t][r] = p;
+      rs += p;
+    }
+  l = fmaf(l, alpha, rs);
+  mc = mc_new;
+#pragma unroll
+  for (int e = 0; e < OB; ++e)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[e][r] *= alpha;
+}
+
+// Epilogue: O / l and LSE for the lane's query row.
+template <int OB>
+__device__ __forceinline__ void store_rows(f32x16 (&o)[OB], float mc, float l, float *orow,
+                                           float *lse, int h, bool valid) {
+  const float lt = pair_sum(l);  // both halves of the row hold partial sums
+  const float inv = 1.0f / lt;
+  if (!valid) return;
+#pragma unroll
+  for (int e = 0; e < OB; ++e)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 v = {o[e][4 * g] * inv, o[e][4 * g + 1] * inv, o[e][4 * g + 2] * inv,
+                 o[e][4 * g + 3] * inv};
+      *reinterpret_cast<f32x4 *>(orow + 32 * e + 8 * g + 4 * h) = v;
+    }
+  if (h == 0) *lse = (mc + lg2(lt)) * kLn2;
+}
+
+// ====================================================================================
+// 16-bit inputs (binary16 or bfloat16), d in {64, 128}
+// ====================================================================================
+template <int D>
+struct Cfg16 {
+  static constexpr int BM = kFusedBM;           // query rows per workgroup
+  static constexpr int BN = D == 128 ? 64 : 128;  // keys per tile
+  static constexpr int ROWB = D * 2;            // bytes per row
+  static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+  static constexpr int TILEB = BN * ROWB;       // 16 KiB per K or V tile
+  static constexpr int CPT = TILEB / 16 / 256;  // chunks per thread per tile
+  static constexpr int QCPT = BM * CPR / 256;   // Q chunks per thread
+  static constexpr int SB = BN / 32;            // 32-key S blocks per tile
+  static constexpr int KC = D / 16;             // k-steps of the Q K product
+  static constexpr int OB = D / 32;             // 32-wide blocks of the output
+  static constexpr int PU = BN / 16;            // k-steps of the P V product
+  static constexpr int LDS = 4 * TILEB;         // K and V, two stages each
+  static_assert(BM * ROWB <= 2 * TILEB, "Q staging must fit in the K stages");
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256, 2) void fa_fwd16_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int N,
+    int nqt, int G, float c) {
+  using C = Cfg16<D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char *const Ks = smem;
+  char *const Vs = smem + 2 * C::TILEB;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int L = xcd_remap(blockIdx.x, G);
+  const int bh = L / nqt, q0 = (L % nqt) * C::BM;
+  const int64_t hoff = int64_t(bh) * N * D;
+  const uint16_t *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff;
+
+  // ---- prologue: Q tile -> LDS (coalesced 16-byte loads) -> registers ----
+#pragma unroll
+  for (int i = 0; i < C::QCPT; ++i) {
+    const int cid = i * 256 + tid, r = cid / C::CPR, ch = cid % C::CPR;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (q0 + r < N) val = *reinterpret_cast<const u32x4 *>(Qh + int64_t(q0 + r) * D + ch * 8);
+    lds_write16(Ks, r * C::ROWB + swz_row<C::CPR>(r, ch) * 16, val);
+  }
+  __syncthreads();
+  u32x4 qf[C::KC];
+  {
+    const int qr = 32 * w + l32;
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc)
+      qf[kc] = lds_read16(Ks, qr * C::ROWB + swz_row<C::CPR>(qr, 2 * kc + h) * 16);
+  }
+  __syncthreads();
+
+  // ---- K/V tile movement: global -> registers -> LDS stage ----
+  u32x4 kreg[C::CPT], vreg[C::CPT];
+  auto fetch = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int cid = i * 256 + tid, r = cid / C::CPR, ch = cid % C::CPR;
+      const int key = kt * C::BN + r;
+      kreg[i] = vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (key < N) {
+        kreg[i] = *reinterpret_cast<const u32x4 *>(Kh + int64_t(key) * D + ch * 8);
+        vreg[i] = *reinterpret_cast<const u32x4 *>(Vh + int64_t(key) * D + ch * 8);
+      }
+    }
+  };
+  auto stage = [&](int buf) {
+    char *kb = Ks + buf * C::TILEB, *vb = Vs + buf * C::TILEB;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int cid = i * 256 + tid, r = cid / C::CPR, ch = cid % C::CPR;
+      lds_write16(kb, r * C::ROWB + swz_row<C::CPR>(r, ch) * 16, kreg[i]);
+      u32x4 vv = vreg[i];
+      if constexpr (BF16) {
+        // the P V product runs in binary16: widen V exactly while staging
+#pragma unroll
+        for (int q = 0; q < 4; ++q) vv[q] = bf16x2_to_f16x2(vv[q]);
+      }
+      lds_write16(vb, r * C::ROWB + swz_v<C::CPR>(r, ch) * 16, vv);
+    }
+  };
+
+  // per-lane offsets of the transposing V reads: lane j of 16-lane group G reads
+  // key row 16u + 8x + 4(G/2) + j/4 at columns 32e + 16(G%2) + 4(j%4) .. +3
+  const int grp = lane >> 4, j16 = lane & 15;
+  const int vrow0 = 4 * (grp >> 1) + (j16 >> 2);
+  const int vcol0 = 16 * (grp & 1) + 4 * (j16 & 3);
+
+  f32x16 o[C::OB];
+#pragma unroll
+  for (int e = 0; e < C::OB; ++e) o[e] = f32x16{};
+  float mc = -INFINITY, l = 0.f;
+
+  const int nkt = (N + C::BN - 1) / C::BN;
+  fetch(0);
+  stage(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    const char *kb = Ks + buf * C::TILEB;
+    const char *vb = Vs + buf * C::TILEB;
+    if (kt + 1 < nkt) fetch(kt + 1);
+
+    // S^T = K Q^T: lane owns query row l32, keys 32t + 8(r/4) + 4h + r%4
+    f32x16 s[C::SB];
+#pragma unroll
+    for (int t = 0; t < C::SB; ++t) {
+      s[t] = f32x16{};
+      const int kr = 32 * t + l32;
+#pragma unroll
+      for (int kc = 0; kc < C::KC; ++kc)
+        s[t] = mma16<BF16>(lds_read16(kb, kr * C::ROWB + swz_row<C::CPR>(kr, 2 * kc + h) * 16),
+                           qf[kc], s[t]);
+    }
+
+    const int nvalid = N - kt * C::BN;
+    if (nvalid < C::BN)
+      softmax_tile<C::SB, C::OB, true>(s, o, mc, l, c, nvalid, h);
+    else
+      softmax_tile<C::SB, C::OB, false>(s, o, mc, l, c, nvalid, h);
+
+    // P -> binary16 operands: step u takes block u/2, registers 8(u%2) .. +7,
+    // i.e. keys 16u + 8x + 4h + s for slot 4x + s
+    u32x4 pf[C::PU];
+#pragma unroll
+    for (int u = 0; u < C::PU; ++u) {
+      const int t = u >> 1, rb = (u & 1) * 8;
+      pf[u] = u32x4{pack_f16(s[t][rb + 0], s[t][rb + 1]), pack_f16(s[t][rb + 2], s[t][rb + 3]),
+                    pack_f16(s[t][rb + 4], s[t][rb + 5]), pack_f16(s[t][rb + 6], s[t][rb + 7])};
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int e = 0; e < C::OB; ++e) {
+      const int col = 32 * e + vcol0;
+      const int ch = col >> 3, cb = (col & 7) * 2;
+#pragma unroll
+      for (int u = 0; u < C::PU; ++u) {
+        const int r0 = 16 * u + vrow0, r1 = r0 + 8;
+        u32x2 a0 = lds_read_tr(vb, r0 * C::ROWB + swz_v<C::CPR>(r0, ch) * 16 + cb);
+        u32x2 a1 = lds_read_tr(vb, r1 * C::ROWB + swz_v<C::CPR>(r1, ch) * 16 + cb);
+        o[e] = mma_f16(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf[u], o[e]);
+      }
+    }
+
+    if (kt + 1 < nkt) stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  const int row = q0 + 32 * w + l32;
+  store_rows<C::OB>(o, mc, l, O + hoff + int64_t(row) * D, LSE + int64_t(bh) * N + row, h,
+                    row < N);
+}
+
+// ====================================================================================
+// fp32 inputs, d in {64, 128}: fp32 matrix cores, fp32 P
+// ====================================================================================
+template <int D>
+struct Cfg32 {
+  static constexpr int BM = kFusedBM;
+  static constexpr int BN = 64;
+  static constexpr int ROWB = D * 4;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int TILEB = BN * ROWB;
+  static constexpr int CPT = TILEB / 16 / 256;
+  static constexpr int QCPT = BM * CPR / 256;
+  static constexpr int SB = BN / 32;
+  static constexpr int KC = D / 8;  // 16-byte chunks per lane half: 4 k-steps each
+  static constexpr int OB = D / 32;
+  static constexpr int LDS = 4 * TILEB;
+  static_assert(BM * ROWB <= 2 * TILEB, "Q staging must fit in the K stages");
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
+    const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
+    float *__restrict__ O, float *__restrict__ LSE, int N, int nqt, int G, float c) {
+  using C = Cfg32<D>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char *const Ks = smem;
+  char *const Vs = smem + 2 * C::TILEB;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int L = xcd_remap(blockIdx.x, G);
+  const int bh = L / nqt, q0 = (L % nqt) * C::BM;
+  const int64_t hoff = int64_t(bh) * N * D;
+  const float *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff;
+
+#pragma unroll
+  for (int i = 0; i < C::QCPT; ++i) {
+    const int cid = i * 256 + tid, r = cid / C::CPR, ch = cid % C::CPR;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (q0 + r < N) val = *reinterpret_cast<const u32x4 *>(Qh + int64_t(q0 + r) * D + ch * 4);
+    lds_write16(Ks, r * C::ROWB + swz_row<C::CPR>(r, ch) * 16, val);
+  }
+  __syncthreads();
+  // k-step 4*kc + i of the Q K product uses column 8kc + 4h + i on both operands
+  f32x4 qf[C::KC];
+  {
+    const int qr = 32 * w + l32;
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc)
+      qf[kc] = __builtin_bit_cast(
+          f32x4, lds_read16(Ks, qr * C::ROWB + swz_row<C::CPR>(qr, 2 * kc + h) * 16));
+  }
+  __syncthreads();
+
+  u32x4 kreg[C::CPT], vreg[C::CPT];
+  auto fetch = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int cid = i * 256 + tid, r = cid / C::CPR, ch = cid % C::CPR;
+      const int key = kt * C::BN + r;
+      kreg[i] = vreg[i] = u32x4{0u, 0u, 0u, 0u};
+      if (key < N) {
+        kreg[i] = *reinterpret_cast<const u32x4 *>(Kh + int64_t(key) * D + ch * 4);
+        vreg[i] = *reinterpret_cast<const u32x4 *>(Vh + int64_t(key) * D + ch * 4);
+      }
+    }
+  };
+  auto stage = [&](int buf) {
+    char *kb = Ks + buf * C::TILEB, *vb = Vs + buf * C::TILEB;
+#pragma unroll
+    for (int i = 0; i < C::CPT; ++i) {
+      const int cid = i * 256 + tid, r = cid / C::CPR, ch = cid % C::CPR;
+      lds_write16(kb, r * C::ROWB + swz_row<C::CPR>(r, ch) * 16, kreg[i]);
+      lds_write16(vb, r * C::ROWB + swz_row<C::CPR>(r, ch) * 16, vreg[i]);
+    }
+  };
+
+  f32x16 o[C::OB];
+#pragma unroll
+  for (int e = 0; e < C::OB; ++e) o[e] = f32x16{};
+  float mc = -INFINITY, l = 0.f;
+
+  const int nkt = (N + C::BN - 1) / C::BN;
+  fetch(0);
+  stage(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    const char *kb = Ks + buf * C::TILEB;
+    const char *vb = Vs + buf * C::TILEB;
+    if (kt + 1 < nkt) fetch(kt + 1);
+
+    f32x16 s[C::SB];
+#pragma unroll
+    for (int t = 0; t < C::SB; ++t) {
+      s[t] = f32x16{};
+      const int kr = 32 * t + l32;
+#pragma unroll
+      for (int kc = 0; kc < C::KC; ++kc) {
+        f32x4 kf = __builtin_bit_cast(
+            f32x4, lds_read16(kb, kr * C::ROWB + swz_row<C::CPR>(kr, 2 * kc + h) * 16));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[t] = mma_f32(kf[i], qf[kc][i], s[t]);
+      }
+    }
+
+    const int nvalid = N - kt * C::BN;
+    if (nvalid < C::BN)
+      softmax_tile<C::SB, C::OB, true>(s, o, mc, l, c, nvalid, h);
+    else
+      softmax_tile<C::SB, C::OB, false>(s, o, mc, l, c, nvalid, h);
+
+    // O^T += V^T P^T, one key pair per step: register r of block t holds, on lane half
+    // h, key 32t + 8(r/4) + 4h + r%4; the V operand is that key's row, column 32e + l32
+#pragma unroll
+    for (int e = 0; e < C::OB; ++e) {
+      const int col = 32 * e + l32, ch = col >> 2, cb = (col & 3) * 4;
+#pragma unroll
+      for (int t = 0; t < C::SB; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+          const float vv =
+              *reinterpret_cast<const float *>(vb + key * C::ROWB + swz_row<C::CPR>(key, ch) * 16 + cb);
+          o[e] = mma_f32(vv, s[t][r], o[e]);
+        }
+    }
+
+    if (kt + 1 < nkt) stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  const int row = q0 + 32 * w + l32;
+  store_rows<C::OB>(o, mc, l, O + hoff + int64_t(row) * D, LSE + int64_t(bh) * N + row, h,
+                    row < N);
+}
+
+// ------------------------------------------------------------------------------------
+template <typename KernelT>
+static hipError_t allow_lds(KernelT kernel, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int D, bool BF16>
+static hipError_t run16(const Problem &p, hipStream_t stream) {
+  using C = Cfg16<D>;
+  auto kern = fa_fwd16_kernel<D, BF16>;
+  // raise the dynamic-LDS cap once; a refusal surfaces as a launch error below
+  static const hipError_t attr = allow_lds(kern, C::LDS);
+  (void)attr;
+  const int nqt = (p.N + C::BM - 1) / C::BM;
+  const int G = nqt * p.B * p.H;
+  const float c = p.scale * kLog2e;
+  hipLaunchKernelGGL(kern, dim3(G), dim3(256), C::LDS, stream,
+                     static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
+                     static_cast<const uint16_t *>(p.v), p.o, p.lse, p.N, nqt, G, c);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t run32(const Problem &p, hipStream_t stream) {
+  using C = Cfg32<D>;
+  auto kern = fa_fwd32_kernel<D>;
+  // raise the dynamic-LDS cap once; a refusal surfaces as a launch error below
+  static const hipError_t attr = allow_lds(kern, C::LDS);
+  (void)attr;
+  const int nqt = (p.N + C::BM - 1) / C::BM;
+  const int G = nqt * p.B * p.H;
+  const float c = p.scale * kLog2e;
+  hipLaunchKernelGGL(kern, dim3(G), dim3(256), C::LDS, stream,
+                     static_cast<const float *>(p.q), static_cast<const float *>(p.k),
+                     static_cast<const float *>(p.v), p.o, p.lse, p.N, nqt, G, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const Problem &p, hipStream_t stream) {
+  switch (p.dtype) {
+    case kF16: return p.d == 128 ? run16<128, false>(p, stream) : run16<64, false>(p, stream);
+    case kBF16: return p.d == 128 ? run16<128, true>(p, stream) : run16<64, true>(p, stream);
+    default: return p.d == 128 ? run32<128>(p, stream) : run32<64>(p, stream);
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,29 @@
+// Internal launch interface between the C boundary (fa_api.cpp) and the kernels.
+// Every launcher assumes its arguments were validated by the boundary: shapes
+// positive, d in {64, 128}, pointers non-null and aligned, grid within limits.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+enum Dtype { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+struct Problem {
+  const void *q, *k, *v;
+  float *o, *lse;
+  int B, H, N, d;
+  float scale;
+  int dtype;
+};
+
+// Query rows per workgroup of the fused kernel (every variant uses 4 waves x 32 rows).
+constexpr int kFusedBM = 128;
+// Largest grid (in workgroups) any launcher issues: 256 threads x 2^24 < 2^32 work-items.
+constexpr int64_t kMaxGrid = int64_t(1) << 24;
+
+hipError_t launch_fused(const Problem &p, hipStream_t stream);
+hipError_t launch_naive(const Problem &p, void *s_ws, void *p_ws, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,132 @@
+/*
+ * fa.h - C boundary of the gfx950 attention forward library (libfa.so).
+ *
+ * The library computes non-causal scaled dot-product attention
+ *
+ *     O = softmax(scale * Q K^T) V,      LSE = log(sum_j exp(scale * q_i . k_j))
+ *
+ * for every batch b, head h and query row i.  The operation is the attention
+ * formula and its three-step standard form in the MUSA SDK guide
+ * "FlashAttention optimization" (sections "Standard attention formula" and
+ * "three-step computation"), computed the way that guide's "FlashAttention
+ * complete algorithm" formula prescribes: Q blocks stay on chip while K/V blocks
+ * stream past, a running row max m and row sum l are kept per query row, the
+ * output accumulator is rescaled by exp(m_old - m_new) before each new P V
+ * block is added, and O / l is written at the end (steps 1-4, a-f).  The
+ * N x N score and probability matrices never reach device memory.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, contiguous, row-major with the head dimension fastest:
+ *       q, k, v : [B, H, N, d] of the input dtype (see fa_dtype)
+ *       o       : [B, H, N, d] float32 (always float32, whatever the input dtype)
+ *       lse     : [B, H, N]    float32, natural logarithm
+ *   - All tensor pointers are device memory owned by the caller.  The library
+ *     never allocates, frees or retains them.
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     enqueue work and return; results are valid once the stream has reached
+ *     the enqueued work (e.g. after hipStreamSynchronize).
+ *   - Argument checks run on the host before anything is enqueued.  On any error
+ *     nothing is launched and outputs are untouched.
+ *   - NaN or Inf inside q, k or v is not checked; it propagates to the outputs.
+ *   - All entry points are thread-safe; the library keeps no mutable state other
+ *     than a per-thread copy of the last HIP error code.
+ */
+#ifndef EXACT_ATTENTION_90_AMD_FA_H
+#define EXACT_ATTENTION_90_AMD_FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Input element type of q, k and v. */
+enum fa_dtype {
+    FA_F32 = 0,  /* IEEE binary32 */
+    FA_F16 = 1,  /* IEEE binary16 */
+    FA_BF16 = 2  /* bfloat16 (upper half of a binary32) */
+};
+
+/* Return codes.  FA_OK is 0; every error is positive. */
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,      /* a required pointer is NULL (and the problem is not empty) */
+    FA_ERR_SHAPE = 2,     /* B, H or N negative, or the problem too large to index */
+    FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
+    FA_ERR_DTYPE = 4,     /* dtype is not one of fa_dtype */
+    FA_ERR_SCALE = 5,     /* scale is not a finite number > 0 */
+    FA_ERR_ALIGN = 6,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+    FA_ERR_WORKSPACE = 7, /* naive path: a workspace pointer is NULL or misaligned */
+    FA_ERR_HIP = 8        /* no usable HIP device, or a launch failed; see fa_last_hip_error */
+};
+
+/*
+ * fa_fwd - fused attention forward (FlashAttention).
+ *
+ *   q, k, v  device pointers, [B, H, N, d] contiguous, element type `dtype`,
+ *            16-byte aligned.
+ *   o        device pointer, [B, H, N, d] float32, 16-byte aligned.  Receives
+ *            O = softmax(scale * Q K^T) V.
+ *   lse      device pointer, [B, H, N] float32, 4-byte aligned.  Receives
+ *            m + ln(l): the natural log of sum_j exp(scale * q_i . k_j).
+ *   B, H, N  batch, heads, sequence length (queries = keys = N).  Any value >= 0;
+ *            N need not be a multiple of any tile size.  If B*H*N == 0 the call
+ *            checks its other arguments and returns FA_OK without launching
+ *            (pointers may then be NULL).
+ *   d        head dimension: 64 or 128.
+ *   scale    softmax scale, finite and > 0 (usually 1/sqrt(d)).  It multiplies
+ *            the float32 dot products; it is never folded into 16-bit inputs.
+ *   dtype    FA_F32, FA_F16 or FA_BF16.
+ *   stream   hipStream_t as void*.
+ *
+ * Precision: products of q and k run on the matrix cores in the input type with
+ * float32 accumulation; softmax statistics are float32.  The probabilities P
+ * enter the P V product as binary16 for FA_F16 and FA_BF16 inputs (for bfloat16
+ * inputs V is widened exactly to binary16 on chip; |v| must stay below 65504)
+ * and as float32 for FA_F32 inputs.  Results are bitwise identical from run to
+ * run for the same inputs and device.
+ *
+ * Returns FA_OK or an fa_status error code.
+ */
+int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int N,
+           int d, float scale, int dtype, void *stream);
+
+/*
+ * fa_naive_fwd - the materialised three-kernel contrast path (not for production).
+ *
+ * Same arguments and outputs as fa_fwd, plus two caller-owned device workspaces
+ * that receive, in the input dtype, the full score matrix S = scale * Q K^T and
+ * the probability matrix P = softmax(S), each [B, H, N, N] row-major
+ * (the standard three steps of the MUSA guide; the Triton tutorial's section 1
+ * sizes these tensors).  Three kernels run in order on `stream`: scores, row
+ * softmax (which also writes lse), and O = P V.  Each kernel accumulates in
+ * float32; S and P are rounded to the input dtype when stored.
+ *
+ *   s_ws, p_ws  device pointers of at least fa_naive_workspace_bytes(B, H, N,
+ *               dtype) bytes each, 16-byte aligned, not overlapping each other
+ *               or any tensor.  NULL or misaligned -> FA_ERR_WORKSPACE.
+ */
+int fa_naive_fwd(const void *q, const void *k, const void *v, float *o, float *lse, void *s_ws,
+                 void *p_ws, int B, int H, int N, int d, float scale, int dtype, void *stream);
+
+/*
+ * Bytes of ONE naive-path workspace: B * H * N * N * sizeof(dtype), rounded up
+ * to a multiple of 256.  Returns 0 for an invalid dtype or a negative size, and
+ * SIZE_MAX if the product does not fit in size_t.
+ */
+size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *fa_status_string(int status);
+
+/* Static version string of the library, e.g. "exact_attention_90_amd 0.1.0 gfx950". */
+const char *fa_version(void);
+
+/* The hipError_t value behind the calling thread's most recent FA_ERR_HIP (0 if none). */
+int fa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_ATTENTION_90_AMD_FA_H */

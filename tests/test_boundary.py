@@ -1,0 +1,115 @@
+"""The C boundary on the CPU: the library loads, exports every declared symbol,
+and rejects bad arguments before touching a device.  No kernel is launched here."""
+import math
+import os
+import re
+
+import pytest
+
+from exact_attention_90_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "page_tensor_sizes.txt")
+CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from exact_attention_90_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_python_export_list():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"libfa.so does not export {name}"
+
+
+def test_status_strings_and_version(lib):
+    for code in range(0, 9):
+        s = lib.fa_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.fa_status_string(99).decode() == "unknown status"
+    assert "gfx950" in lib.fa_version().decode()
+    assert lib.fa_last_hip_error() == 0
+
+
+def test_workspace_bytes_pinned_to_page_sizes(lib):
+    for line in open(GOLDEN):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        fields, cite = line.split("|")
+        B, H, N, dt, printed, tol = fields.split()
+        got = lib.fa_naive_workspace_bytes(int(B), int(H), int(N), CODES[dt])
+        printed = float(printed)
+        assert abs(got - printed) <= float(tol) * printed, (cite, got, printed)
+
+
+def test_workspace_bytes_edges(lib):
+    assert lib.fa_naive_workspace_bytes(1, 1, 3, 1) == 256      # 18 bytes rounded up
+    assert lib.fa_naive_workspace_bytes(0, 5, 7, 0) == 0
+    assert lib.fa_naive_workspace_bytes(1, 1, 1, 7) == 0        # bad dtype
+    assert lib.fa_naive_workspace_bytes(-1, 1, 1, 0) == 0
+    big = lib.fa_naive_workspace_bytes(2**31 - 1, 2**31 - 1, 2**31 - 1, 0)
+    assert big == 2**64 - 1                                     # does not fit size_t
+
+
+# fake, never-dereferenced device addresses (16-byte aligned, non-null)
+A, B_, C_, O_, L_ = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000
+
+
+def call(lib, q=A, k=B_, v=C_, o=O_, lse=L_, B=1, H=1, N=128, d=64, scale=0.125, dtype=1):
+    return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(dtype=3), 4), (dict(dtype=-1), 4),
+    (dict(d=96), 3), (dict(d=0), 3), (dict(d=256), 3),
+    (dict(scale=0.0), 5), (dict(scale=-0.1), 5), (dict(scale=math.inf), 5), (dict(scale=math.nan), 5),
+    (dict(B=-1), 2), (dict(H=-2), 2), (dict(N=-5), 2),
+    (dict(q=None), 1), (dict(v=None), 1), (dict(lse=None), 1),
+    (dict(q=A + 8), 6), (dict(o=O_ + 4), 6), (dict(lse=L_ + 2), 6),
+    (dict(B=2**20, H=2**10, N=2**12), 2),                    # grid beyond 2^24 workgroups
+    (dict(B=2**16, H=2**16, N=1), 2),                        # B*H beyond int
+])
+def test_fwd_rejects_bad_arguments_before_any_device_call(lib, kwargs, code):
+    assert call(lib, **kwargs) == code
+
+
+@pytest.mark.parametrize("kwargs", [dict(N=0), dict(B=0), dict(H=0),
+                                    dict(N=0, q=None, k=None, v=None, o=None, lse=None)])
+def test_empty_problem_is_a_no_op(lib, kwargs):
+    assert call(lib, **kwargs) == 0
+
+
+def test_naive_rejects_bad_workspace(lib):
+    args = (A, B_, C_, O_, L_)
+    assert lib.fa_naive_fwd(*args, None, 0x6000, 1, 1, 64, 64, 0.125, 1, None) == 7
+    assert lib.fa_naive_fwd(*args, 0x6004, 0x7000, 1, 1, 64, 64, 0.125, 1, None) == 7
+    assert lib.fa_naive_fwd(*args, 0x6000, 0x7000, 1, 1, 64, 100, 0.125, 1, None) == 3
+    assert lib.fa_naive_fwd(*args, None, None, 1, 1, 0, 64, 0.125, 1, None) == 0
+
+
+def _gpu_present():
+    return os.path.exists("/dev/kfd")
+
+
+@pytest.mark.skipif(_gpu_present(), reason="only meaningful on a host without a GPU")
+def test_valid_call_without_a_device_reports_hip_error(lib):
+    # every check passes, so the library asks HIP for a device, finds none and
+    # returns FA_ERR_HIP without launching anything
+    assert call(lib) == 8
+    assert lib.fa_last_hip_error() != 0

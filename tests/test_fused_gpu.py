@@ -1,0 +1,156 @@
+"""Parity of the fused HIP kernel (fa_fwd) with the CPU fp64 oracle.
+
+Bar: max |O - O_ref| <= 1e-5 for fp32 inputs and <= 1e-2 (cosine >= 0.999) for
+fp16/bf16 inputs; LSE within 1e-4 relative.  Small problems are compared element
+by element in full; the five named workloads run at full size and are compared on
+sampled rows computed one by one by the oracle.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth.configs import PAGE_WORKLOADS, WORKLOADS
+from synth.inputs import make_qkv, quantize, to_float32
+from tests.gpu_util import (assert_parity, full_case, metrics, run, sample_rows, say,
+                            to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+# ---- small problems, every element ------------------------------------------------
+@pytest.mark.parametrize("B,H,N,d,dtype", [
+    (2, 3, 333, 128, "f16"), (2, 3, 333, 128, "bf16"), (1, 2, 333, 64, "f16"),
+    (1, 2, 333, 64, "bf16"), (2, 2, 200, 64, "f32"), (1, 2, 300, 128, "f32"),
+    (1, 2, 512, 128, "bf16"), (1, 2, 512, 64, "f16"), (1, 1, 1000, 128, "f16"),
+])
+def test_small_full(B, H, N, d, dtype):
+    m, _, _ = full_case(B, H, N, d, dtype, seed=N + d)
+    assert_parity(m, dtype, where=f"{B}x{H}x{N}x{d} {dtype}")
+
+
+def test_c1_tiny_fp32_full():
+    w = WORKLOADS["c1"]
+    m, _, _ = full_case(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.mult)
+    assert_parity(m, w.dtype, where="c1")
+
+
+@pytest.mark.parametrize("name", sorted(PAGE_WORKLOADS))
+def test_page_workloads(name):
+    w = PAGE_WORKLOADS[name]
+    m, _, _ = full_case(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.mult)
+    assert_parity(m, w.dtype, where=name)
+
+
+@pytest.mark.parametrize("N,d", [(64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_single_key_tile(N, d, dtype):
+    # N equal to one key tile: the loop runs once (the tutorial's N_CTX = BLOCK_N check)
+    m, _, _ = full_case(1, 2, N, d, dtype, seed=5)
+    assert_parity(m, dtype, where=f"single tile N={N} d={d}")
+
+
+@pytest.mark.parametrize("N", [1, 2, 3, 31, 33, 127, 129])
+@pytest.mark.parametrize("dtype,d", [("f16", 128), ("bf16", 64), ("f32", 64)])
+def test_tiny_and_ragged(N, dtype, d):
+    m, x, (o, lse) = full_case(1, 3, N, d, dtype, seed=100 + N)
+    assert_parity(m, dtype, where=f"N={N}")
+    if N == 1:
+        # one key: O is that key's value row.  16-bit P rounds 2^(fma residue) to exactly
+        # 1, so O = v (bf16 values below binary16's normal range round when widened for
+        # the P V product); fp32 P keeps the residue of s*c, a relative 2^-24, so O = v
+        # within an ulp or two.
+        v = to_float32(x["v"], dtype).astype(np.float64)
+        err = np.abs(o.cpu().numpy().astype(np.float64) - v).max()
+        tol = {"f16": 0.0, "bf16": 2.0**-25, "f32": 2.0**-22 * np.abs(v).max()}[dtype]
+        assert err <= tol
+
+
+@pytest.mark.parametrize("dtype,mult", [("bf16", 3.0), ("f16", 8.0), ("bf16", 12.0)])
+def test_large_logits(dtype, mult):
+    # logit standard deviation ~ mult^2: needs the running-max subtraction and rescale
+    m, _, _ = full_case(1, 2, 2000, 128, dtype, seed=77, mult=mult)
+    assert_parity(m, dtype, where=f"x{mult}")
+
+
+def test_empty_problem():
+    import torch
+
+    import exact_attention_90_amd as fa
+
+    q = torch.empty((2, 3, 0, 128), dtype=torch.bfloat16, device="cuda")
+    o, lse = fa.fwd(q, q, q)
+    assert o.shape == (2, 3, 0, 128) and lse.shape == (2, 3, 0)
+
+
+# ---- closed forms and invariants on the GPU ------------------------------------------
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("f32", 128)])
+def test_zero_query_gives_column_mean(dtype, d):
+    B, H, N = 2, 2, 777
+    x = make_qkv(B, H, N, d, dtype, seed=8)
+    x["q"] = quantize(np.zeros((B, H, N, d), np.float32), dtype)
+    say(f"Q=0 {dtype} d={d}")
+    o, lse = run("fused", to_device(x, dtype), 1.0 / math.sqrt(d))
+    mean = to_float32(x["v"], dtype).astype(np.float64).mean(axis=2, keepdims=True)
+    tol = 1e-5 if dtype == "f32" else 2e-3
+    assert np.abs(o.cpu().numpy() - mean).max() <= tol
+    assert np.abs(lse.cpu().numpy() - math.log(N)).max() <= 1e-4 * math.log(N)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_constant_v_returns_the_constant(dtype):
+    B, H, N, d = 1, 2, 555, 128
+    x = make_qkv(B, H, N, d, dtype, seed=9, mult=3.0)
+    c = 1.75
+    x["v"] = quantize(np.full((B, H, N, d), c, np.float32), dtype)
+    say(f"V=const {dtype}")
+    o, _ = run("fused", to_device(x, dtype), 1.0 / math.sqrt(d))
+    tol = 1e-5 if dtype == "f32" else 2e-3
+    assert np.abs(o.cpu().numpy() - c).max() <= tol
+
+
+def test_joint_kv_permutation_invariance():
+    B, H, N, d, dtype = 1, 2, 640, 128, "bf16"
+    x = make_qkv(B, H, N, d, dtype, seed=10)
+    say("permutation")
+    o1, l1 = run("fused", to_device(x, dtype), 1.0 / math.sqrt(d))
+    perm = np.random.Generator(np.random.PCG64(3)).permutation(N)
+    xp = dict(q=x["q"], k=np.ascontiguousarray(x["k"][:, :, perm]),
+              v=np.ascontiguousarray(x["v"][:, :, perm]))
+    o2, l2 = run("fused", to_device(xp, dtype), 1.0 / math.sqrt(d))
+    assert np.abs(o1.cpu().numpy() - o2.cpu().numpy()).max() <= 2e-3
+    assert np.abs(l1.cpu().numpy() - l2.cpu().numpy()).max() <= 1e-4 * 10
+
+
+def test_bitwise_deterministic():
+    import torch
+
+    B, H, N, d, dtype = 2, 4, 1024, 128, "bf16"
+    xd = to_device(make_qkv(B, H, N, d, dtype, seed=12), dtype)
+    say("determinism")
+    outs = [run("fused", xd, 1.0 / math.sqrt(d)) for _ in range(3)]
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+
+
+# ---- the named workloads at full size, sampled rows -----------------------------------
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_workload_full_size_sampled(name):
+    w = WORKLOADS[name]
+    scale32 = float(np.float32(w.scale))
+    say(f"{name}: generating {w.short()}")
+    x = make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.mult)
+    say(f"{name}: fused kernel")
+    o, lse = run("fused", to_device(x, w.dtype), scale32)
+    rows = sample_rows(w.B, w.H, w.N)
+    o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], w.dtype, scale32, rows=rows)
+    import torch
+
+    idx = torch.from_numpy(rows).to(o.device)
+    o_s = o.reshape(-1, w.d).index_select(0, idx).cpu().numpy()
+    l_s = lse.reshape(-1).index_select(0, idx).cpu().numpy()
+    m = metrics(o_s, l_s, o_ref, lse_ref)
+    say(f"{name}: {m}")
+    assert_parity(m, w.dtype, where=name)
+    assert bool(np.isfinite(o.cpu().numpy()).all())
