@@ -109,6 +109,21 @@ def cpu_baseline(x, w, o_gpu, lse_gpu, target_s: float):
     return base, parity
 
 
+def copy_calibration(mib: int, steps: int) -> int:
+    """Copy `mib` MiB device-to-device `steps` times: each launch reads and writes
+    exactly mib * 2^20 bytes, which calibrates the memory-traffic counters."""
+    import torch
+
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": steps}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,7 +133,12 @@ def main() -> int:
     ap.add_argument("--path", default="fused", choices=["fused", "naive"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run device-to-device copies of MIB MiB (a "
+                         "plain copy of known size that scales the FETCH/WRITE counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration, max(1, args.steps))
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -38,6 +38,8 @@ int check_args(const void *q, const void *k, const void *v, const float *o, cons
   if (heads > std::numeric_limits<int>::max()) return FA_ERR_SHAPE;
   const int64_t qtiles = (int64_t(N) + fa::kFusedBM - 1) / fa::kFusedBM;
   if (heads * qtiles > fa::kMaxGrid) return FA_ERR_SHAPE;
+  // one head's [N, d] slice is addressed with 32-bit byte offsets (plus one tile)
+  if (int64_t(N) * d * elem_bytes(dtype) > fa::kMaxHeadBytes) return FA_ERR_SHAPE;
   return FA_OK;
 }
 

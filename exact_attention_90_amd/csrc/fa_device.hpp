@@ -116,6 +116,18 @@ __device__ __forceinline__ int swz_v(int r, int ch) {
     return ch ^ ((r & 3) << 2);
 }
 
+// ---- bounds-checked global loads ----------------------------------------------------
+// A raw buffer resource over `bytes` bytes from `base`: 16-byte loads at byte offsets
+// at or beyond `bytes` return zeros instead of touching memory, which pads the ragged
+// last tile of a head.  The third resource word selects 32-bit elements (gfx9 family).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 __device__ __forceinline__ u32x4 lds_read16(const char *base, int byte_off) {
   return *reinterpret_cast<const u32x4 *>(base + byte_off);
 }

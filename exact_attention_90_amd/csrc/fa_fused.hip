@@ -22,6 +22,8 @@
 // rescale factor alpha is a per-lane scalar.  The P registers feed the P V product
 // directly; V stays row-major in LDS and its operand is fetched with the
 // transposing LDS load in the same key order the P registers hold.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -67,10 +69,14 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[SB], f32x16 (&o)[OB], f
     }
   l = fmaf(l, alpha, rs);
   mc = mc_new;
+  // O = alpha O.  When no row of the wave raised its max, every alpha is exactly 1 and
+  // the multiply is the identity: skip it (the result is bitwise the same).
+  if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-  for (int e = 0; e < OB; ++e)
+    for (int e = 0; e < OB; ++e)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[e][r] *= alpha;
+      for (int r = 0; r < 16; ++r) o[e][r] *= alpha;
+  }
 }
 
 // Epilogue: O / l and LSE for the lane's query row.
@@ -97,10 +103,10 @@ __device__ __forceinline__ void store_rows(f32x16 (&o)[OB], float mc, float l, f
 template <int D>
 struct Cfg16 {
   static constexpr int BM = kFusedBM;           // query rows per workgroup
-  static constexpr int BN = D == 128 ? 64 : 128;  // keys per tile
+  static constexpr int BN = 64;                 // keys per tile
   static constexpr int ROWB = D * 2;            // bytes per row
   static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
-  static constexpr int TILEB = BN * ROWB;       // 16 KiB per K or V tile
+  static constexpr int TILEB = BN * ROWB;       // bytes of one K or V tile
   static constexpr int CPT = TILEB / 16 / 256;  // chunks per thread per tile
   static constexpr int QCPT = BM * CPR / 256;   // Q chunks per thread
   static constexpr int SB = BN / 32;            // 32-key S blocks per tile
@@ -126,15 +132,23 @@ __global__ __launch_bounds__(256, 2) void fa_fwd16_kernel(
   const int L = xcd_remap(blockIdx.x, G);
   const int bh = L / nqt, q0 = (L % nqt) * C::BM;
   const int64_t hoff = int64_t(bh) * N * D;
-  const uint16_t *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff;
+  // buffer resources over this head's [N, D] slices: loads past row N - 1 read zeros
+  const uint32_t head_bytes = uint32_t(N) * C::ROWB;
+  const auto qrs = make_rsrc(Q + hoff, head_bytes);
+  const auto krs = make_rsrc(K + hoff, head_bytes);
+  const auto vrs = make_rsrc(V + hoff, head_bytes);
+  constexpr int ST_STEP = 256 * 16;  // bytes between a thread's chunks, in LDS and in memory
+  // A tile of rows is one contiguous block of global memory: thread tid moves the
+  // 16-byte chunks tid + 256 i.  Their LDS rows differ by 256/CPR per i, which leaves
+  // the swizzle key unchanged, so one lane offset plus immediates addresses them all.
+  const int srow = tid / C::CPR, sch = tid % C::CPR;
 
   // ---- prologue: Q tile -> LDS (coalesced 16-byte loads) -> registers ----
+  {
+    const int st_q = srow * C::ROWB + swz_row<C::CPR>(srow, sch) * 16;
 #pragma unroll
-  for (int i = 0; i < C::QCPT; ++i) {
-    const int cid = i * 256 + tid, r = cid / C::CPR, ch = cid % C::CPR;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (q0 + r < N) val = *reinterpret_cast<const u32x4 *>(Qh + int64_t(q0 + r) * D + ch * 8);
-    lds_write16(Ks, r * C::ROWB + swz_row<C::CPR>(r, ch) * 16, val);
+    for (int i = 0; i < C::QCPT; ++i)
+      lds_write16(Ks, st_q + i * ST_STEP, buf_load16(qrs, tid * 16, q0 * C::ROWB + i * ST_STEP));
   }
   __syncthreads();
   u32x4 qf[C::KC];
@@ -146,41 +160,47 @@ __global__ __launch_bounds__(256, 2) void fa_fwd16_kernel(
   }
   __syncthreads();
 
+  // ---- per-lane LDS offsets, fixed for the whole loop ----
+  const int st_k = srow * C::ROWB + swz_row<C::CPR>(srow, sch) * 16;
+  const int st_v = srow * C::ROWB + swz_v<C::CPR>(srow, sch) * 16;
+  // K operand rows 32t + l32: the swizzle key depends on l32 only
+  int kofs[C::KC];
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc) kofs[kc] = l32 * C::ROWB + swz_row<C::CPR>(l32, 2 * kc + h) * 16;
+  // transposing V reads: lane j of 16-lane group G reads key row 16u + 8x + 4(G/2) + j/4
+  // at columns 32e + 16(G%2) + 4(j%4); the swizzle key depends on the lane only
+  const int grp = lane >> 4, j16 = lane & 15;
+  const int vrow0 = 4 * (grp >> 1) + (j16 >> 2);
+  const int vcol0 = 16 * (grp & 1) + 4 * (j16 & 3);
+  int vofs[C::OB];
+#pragma unroll
+  for (int e = 0; e < C::OB; ++e) {
+    const int col = 32 * e + vcol0;
+    vofs[e] = vrow0 * C::ROWB + swz_v<C::CPR>(vrow0, col >> 3) * 16 + (col & 7) * 2;
+  }
+
   // ---- K/V tile movement: global -> registers -> LDS stage ----
   u32x4 kreg[C::CPT], vreg[C::CPT];
   auto fetch = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const int cid = i * 256 + tid, r = cid / C::CPR, ch = cid % C::CPR;
-      const int key = kt * C::BN + r;
-      kreg[i] = vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (key < N) {
-        kreg[i] = *reinterpret_cast<const u32x4 *>(Kh + int64_t(key) * D + ch * 8);
-        vreg[i] = *reinterpret_cast<const u32x4 *>(Vh + int64_t(key) * D + ch * 8);
-      }
+      kreg[i] = buf_load16(krs, tid * 16, kt * C::TILEB + i * ST_STEP);
+      vreg[i] = buf_load16(vrs, tid * 16, kt * C::TILEB + i * ST_STEP);
     }
   };
-  auto stage = [&](int buf) {
-    char *kb = Ks + buf * C::TILEB, *vb = Vs + buf * C::TILEB;
+  auto stage = [&](char *kb, char *vb) {
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const int cid = i * 256 + tid, r = cid / C::CPR, ch = cid % C::CPR;
-      lds_write16(kb, r * C::ROWB + swz_row<C::CPR>(r, ch) * 16, kreg[i]);
+      lds_write16(kb, st_k + i * ST_STEP, kreg[i]);
       u32x4 vv = vreg[i];
       if constexpr (BF16) {
         // the P V product runs in binary16: widen V exactly while staging
 #pragma unroll
         for (int q = 0; q < 4; ++q) vv[q] = bf16x2_to_f16x2(vv[q]);
       }
-      lds_write16(vb, r * C::ROWB + swz_v<C::CPR>(r, ch) * 16, vv);
+      lds_write16(vb, st_v + i * ST_STEP, vv);
     }
   };
-
-  // per-lane offsets of the transposing V reads: lane j of 16-lane group G reads
-  // key row 16u + 8x + 4(G/2) + j/4 at columns 32e + 16(G%2) + 4(j%4) .. +3
-  const int grp = lane >> 4, j16 = lane & 15;
-  const int vrow0 = 4 * (grp >> 1) + (j16 >> 2);
-  const int vcol0 = 16 * (grp & 1) + 4 * (j16 & 3);
 
   f32x16 o[C::OB];
 #pragma unroll
@@ -188,26 +208,24 @@ __global__ __launch_bounds__(256, 2) void fa_fwd16_kernel(
   float mc = -INFINITY, l = 0.f;
 
   const int nkt = (N + C::BN - 1) / C::BN;
-  fetch(0);
-  stage(0);
-  __syncthreads();
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    const char *kb = Ks + buf * C::TILEB;
-    const char *vb = Vs + buf * C::TILEB;
-    if (kt + 1 < nkt) fetch(kt + 1);
+  // one key tile: BUF is the LDS stage holding it (compile-time, so every LDS address
+  // below is a lane register plus an immediate)
+  auto tile = [&](auto bufc, int kt) {
+    constexpr int BUF = decltype(bufc)::value;
+    const char *kb = Ks + BUF * C::TILEB;
+    const char *vb = Vs + BUF * C::TILEB;
+    const bool more = kt + 1 < nkt;
+    if (more) fetch(kt + 1);
 
     // S^T = K Q^T: lane owns query row l32, keys 32t + 8(r/4) + 4h + r%4
     f32x16 s[C::SB];
 #pragma unroll
     for (int t = 0; t < C::SB; ++t) {
       s[t] = f32x16{};
-      const int kr = 32 * t + l32;
 #pragma unroll
       for (int kc = 0; kc < C::KC; ++kc)
-        s[t] = mma16<BF16>(lds_read16(kb, kr * C::ROWB + swz_row<C::CPR>(kr, 2 * kc + h) * 16),
-                           qf[kc], s[t]);
+        s[t] = mma16<BF16>(lds_read16(kb, kofs[kc] + 32 * t * C::ROWB), qf[kc], s[t]);
     }
 
     const int nvalid = N - kt * C::BN;
@@ -228,20 +246,24 @@ __global__ __launch_bounds__(256, 2) void fa_fwd16_kernel(
 
     // O^T += V^T P^T
 #pragma unroll
-    for (int e = 0; e < C::OB; ++e) {
-      const int col = 32 * e + vcol0;
-      const int ch = col >> 3, cb = (col & 7) * 2;
+    for (int e = 0; e < C::OB; ++e)
 #pragma unroll
       for (int u = 0; u < C::PU; ++u) {
-        const int r0 = 16 * u + vrow0, r1 = r0 + 8;
-        u32x2 a0 = lds_read_tr(vb, r0 * C::ROWB + swz_v<C::CPR>(r0, ch) * 16 + cb);
-        u32x2 a1 = lds_read_tr(vb, r1 * C::ROWB + swz_v<C::CPR>(r1, ch) * 16 + cb);
+        u32x2 a0 = lds_read_tr(vb, vofs[e] + (16 * u) * C::ROWB);
+        u32x2 a1 = lds_read_tr(vb, vofs[e] + (16 * u + 8) * C::ROWB);
         o[e] = mma_f16(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf[u], o[e]);
       }
-    }
 
-    if (kt + 1 < nkt) stage(buf ^ 1);
+    if (more) stage(Ks + (BUF ^ 1) * C::TILEB, Vs + (BUF ^ 1) * C::TILEB);
     __syncthreads();
+  };
+
+  fetch(0);
+  stage(Ks, Vs);
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += 2) {
+    tile(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < nkt) tile(std::integral_constant<int, 1>{}, kt + 1);
   }
 
   const int row = q0 + 32 * w + l32;

@@ -22,6 +22,9 @@ struct Problem {
 constexpr int kFusedBM = 128;
 // Largest grid (in workgroups) any launcher issues: 256 threads x 2^24 < 2^32 work-items.
 constexpr int64_t kMaxGrid = int64_t(1) << 24;
+// Largest [N, d] slice of one head, in bytes: kernels address a head with 32-bit byte
+// offsets and may read one tile (<= 64 KiB) past its end (those reads return zeros).
+constexpr int64_t kMaxHeadBytes = (int64_t(1) << 31) - (int64_t(1) << 17);
 
 hipError_t launch_fused(const Problem &p, hipStream_t stream);
 hipError_t launch_naive(const Problem &p, void *s_ws, void *p_ws, hipStream_t stream);

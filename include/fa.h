@@ -51,7 +51,8 @@ enum fa_dtype {
 enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL = 1,      /* a required pointer is NULL (and the problem is not empty) */
-    FA_ERR_SHAPE = 2,     /* B, H or N negative, or the problem too large to index */
+    FA_ERR_SHAPE = 2,     /* B, H or N negative, or too large: B*H*ceil(N/128) > 2^24
+                             workgroups, or one head's N*d*elem > 2^31 - 2^17 bytes */
     FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
     FA_ERR_DTYPE = 4,     /* dtype is not one of fa_dtype */
     FA_ERR_SCALE = 5,     /* scale is not a finite number > 0 */

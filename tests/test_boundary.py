@@ -84,6 +84,7 @@ def call(lib, q=A, k=B_, v=C_, o=O_, lse=L_, B=1, H=1, N=128, d=64, scale=0.125,
     (dict(q=A + 8), 6), (dict(o=O_ + 4), 6), (dict(lse=L_ + 2), 6),
     (dict(B=2**20, H=2**10, N=2**12), 2),                    # grid beyond 2^24 workgroups
     (dict(B=2**16, H=2**16, N=1), 2),                        # B*H beyond int
+    (dict(N=2**23, d=128, dtype=1), 2),                      # one head beyond 2^31 bytes
 ])
 def test_fwd_rejects_bad_arguments_before_any_device_call(lib, kwargs, code):
     assert call(lib, **kwargs) == code
