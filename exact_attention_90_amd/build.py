@@ -21,6 +21,8 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of every device code object.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-file code-generation choices (none at present).
+FILE_FLAGS = {}
 
 
 def hipcc() -> str:
@@ -37,7 +39,8 @@ def build(report: bool = False, verbose: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-               "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS, "-c",
+               "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS,
+               *FILE_FLAGS.get(src, []), "-c",
                os.path.join(CSRC, src), "-o", obj]
         if report:
             cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")

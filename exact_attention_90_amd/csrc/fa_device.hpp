@@ -117,9 +117,10 @@ __device__ __forceinline__ int swz_v(int r, int ch) {
 }
 
 // ---- bounds-checked global loads ----------------------------------------------------
-// A raw buffer resource over `bytes` bytes from `base`: 16-byte loads at byte offsets
-// at or beyond `bytes` return zeros instead of touching memory, which pads the ragged
-// last tile of a head.  The third resource word selects 32-bit elements (gfx9 family).
+// A raw buffer resource over `bytes` bytes from `base`: 16-byte loads whose byte offset
+// (VGPR offset + SGPR offset, both range-checked on gfx950) is at or beyond `bytes`
+// return zeros without touching memory, which pads the ragged last tile of a head.
+// The third resource word selects 32-bit elements (gfx9 family).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
                                            0x00020000);

@@ -1,0 +1,90 @@
+// Online-softmax and epilogue building blocks shared by the fused attention kernels.
+#pragma once
+
+#include "fa_device.hpp"
+
+namespace fa {
+
+// ------------------------------------------------------------------------------------
+// Online softmax over one key tile (shared by the 16-bit and fp32 variants).
+//   s[SB]   scores of the tile (S^T blocks of 32 keys), replaced by P in place
+//   o[OB]   output accumulator, rescaled by alpha
+//   mc, l   running max (pre-multiplied by c) and this lane's partial row sum
+//   nvalid  number of valid keys in the tile (keys >= nvalid are masked to -inf)
+//   SKIP    skip the O multiply when every alpha of the wave is 1 (a wave-uniform
+//           branch); false keeps the tile body branch-free for instruction scheduling
+// ------------------------------------------------------------------------------------
+template <int SB, int OB, bool MASK, bool SKIP = true>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[SB], f32x16 (&o)[OB], float &mc, float &l,
+                                             float c, int nvalid, int h) {
+  if constexpr (MASK) {
+#pragma unroll
+    for (int t = 0; t < SB; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key >= nvalid) s[t][r] = -INFINITY;
+      }
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int t = 0; t < SB; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+  mx = pair_max(mx);                       // full row max over the tile's keys
+  const float mc_new = fmaxf(mc, mx * c);  // running max in base-2 units
+  // a row that has seen only masked keys keeps alpha = 0 and P = 0 (no inf - inf)
+  const float alpha = (mc == -INFINITY) ? 0.f : ex2(mc - mc_new);
+  const float sub = (mc_new == -INFINITY) ? 0.f : mc_new;
+  float rs = 0.f;
+#pragma unroll
+  for (int t = 0; t < SB; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = ex2(fmaf(s[t][r], c, -sub));
+      s[t][r] = p;
+      rs += p;
+    }
+  l = fmaf(l, alpha, rs);
+  mc = mc_new;
+  // O = alpha O.  When no row of the wave raised its max, every alpha is exactly 1 and
+  // the multiply is the identity: skip it (the result is bitwise the same).
+  if (!SKIP || __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+    for (int e = 0; e < OB; ++e)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[e][r] *= alpha;
+  }
+}
+
+// P (fp32, in the S^T register layout) -> binary16 operands of the P V product:
+// step u takes S block u/2, registers 8(u%2) .. +7, i.e. keys 16u + 8x + 4h + s in
+// slot 4x + s
+template <int SB>
+__device__ __forceinline__ void pack_p(const f32x16 (&s)[SB], u32x4 (&pf)[2 * SB]) {
+#pragma unroll
+  for (int u = 0; u < 2 * SB; ++u) {
+    const int t = u >> 1, rb = (u & 1) * 8;
+    pf[u] = u32x4{pack_f16(s[t][rb + 0], s[t][rb + 1]), pack_f16(s[t][rb + 2], s[t][rb + 3]),
+                  pack_f16(s[t][rb + 4], s[t][rb + 5]), pack_f16(s[t][rb + 6], s[t][rb + 7])};
+  }
+}
+// Epilogue: O / l and LSE for the lane's query row.
+template <int OB>
+__device__ __forceinline__ void store_rows(f32x16 (&o)[OB], float mc, float l, float *orow,
+                                           float *lse, int h, bool valid) {
+  const float lt = pair_sum(l);  // both halves of the row hold partial sums
+  const float inv = 1.0f / lt;
+  if (!valid) return;
+#pragma unroll
+  for (int e = 0; e < OB; ++e)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 v = {o[e][4 * g] * inv, o[e][4 * g + 1] * inv, o[e][4 * g + 2] * inv,
+                 o[e][4 * g + 3] * inv};
+      *reinterpret_cast<f32x4 *>(orow + 32 * e + 8 * g + 4 * h) = v;
+    }
+  if (h == 0) *lse = (mc + lg2(lt)) * kLn2;
+}
+
+}  // namespace fa
