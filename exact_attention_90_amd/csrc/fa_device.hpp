@@ -129,6 +129,16 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+// 16 bytes per lane from global memory straight into LDS, without passing through
+// registers: lane l of the wave writes lds_wave_base + 16 l (lds_wave_base is uniform
+// across the wave).  Out-of-range dwords are written as zeros.  Completion is counted
+// by vmcnt like any other global load.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char *lds_wave_base,
+                                               int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void *)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 lds_read16(const char *base, int byte_off) {
   return *reinterpret_cast<const u32x4 *>(base + byte_off);
 }

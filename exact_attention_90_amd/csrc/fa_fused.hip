@@ -111,26 +111,35 @@ __global__ __launch_bounds__(256, 2) void fa_fwd16_kernel(
     vofs[e] = vrow0 * C::ROWB + swz_v<C::CPR>(vrow0, col >> 3) * 16 + (col & 7) * 2;
   }
 
-  // ---- K/V tile movement: global -> registers -> LDS stage ----
-  u32x4 kreg[C::CPT], vreg[C::CPT];
-  auto fetch = [&](int kt) {
+  // ---- K/V tile movement ----
+  // K (and V for binary16 inputs) go from global memory straight into an LDS stage.
+  // LDS byte 16 c of a stage is written by lane c % 64 of wave (c / 64) % 4, instruction
+  // c / 256; that position holds logical chunk swz(row, c % CPR) of row c / CPR, and since
+  // each swizzle is an involution the lane's global offset within the tile is its st_k /
+  // st_v value.  bfloat16 V passes through registers so it can be widened to binary16.
+  const int dma_wave = __builtin_amdgcn_readfirstlane(w) * 1024;  // wave's 1 KiB of a step
+  [[maybe_unused]] u32x4 vreg[C::CPT];
+  auto fetch = [&](int kt, char *kb, char *vb) {
+    const int toff = kt * C::TILEB;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      kreg[i] = buf_load16(krs, tid * 16, kt * C::TILEB + i * ST_STEP);
-      vreg[i] = buf_load16(vrs, tid * 16, kt * C::TILEB + i * ST_STEP);
+      buf_load16_lds(krs, kb + dma_wave + i * ST_STEP, st_k, toff + i * ST_STEP);
+      if constexpr (BF16)
+        vreg[i] = buf_load16(vrs, tid * 16, toff + i * ST_STEP);
+      else
+        buf_load16_lds(vrs, vb + dma_wave + i * ST_STEP, st_v, toff + i * ST_STEP);
     }
   };
-  auto stage = [&](char *kb, char *vb) {
+  auto stage = [&](char *vb) {
+    if constexpr (BF16) {
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      lds_write16(kb, st_k + i * ST_STEP, kreg[i]);
-      u32x4 vv = vreg[i];
-      if constexpr (BF16) {
-        // the P V product runs in binary16: widen V exactly while staging
+      for (int i = 0; i < C::CPT; ++i) {
+        // the P V product runs in binary16: widen V while staging
+        u32x4 vv = vreg[i];
 #pragma unroll
         for (int q = 0; q < 4; ++q) vv[q] = bf16x2_to_f16x2(vv[q]);
+        lds_write16(vb, st_v + i * ST_STEP, vv);
       }
-      lds_write16(vb, st_v + i * ST_STEP, vv);
     }
   };
 
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd16_kernel(
     const char *kb = Ks + BUF * C::TILEB;
     const char *vb = Vs + BUF * C::TILEB;
     const bool more = kt + 1 < nkt;
-    if (more) fetch(kt + 1);
+    if (more) fetch(kt + 1, Ks + (BUF ^ 1) * C::TILEB, Vs + (BUF ^ 1) * C::TILEB);
 
     // S^T = K Q^T: lane owns query row l32, keys 32t + 8(r/4) + 4h + r%4
     f32x16 s[C::SB];
@@ -186,12 +195,12 @@ __global__ __launch_bounds__(256, 2) void fa_fwd16_kernel(
         o[e] = mma_f16(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf[u], o[e]);
       }
 
-    if (more) stage(Ks + (BUF ^ 1) * C::TILEB, Vs + (BUF ^ 1) * C::TILEB);
-    __syncthreads();
+    if (more) stage(Vs + (BUF ^ 1) * C::TILEB);
+    __syncthreads();  // also waits for this wave's loads into the other stage
   };
 
-  fetch(0);
-  stage(Ks, Vs);
+  fetch(0, Ks, Vs);
+  stage(Vs);
   __syncthreads();
   for (int kt = 0; kt < nkt; kt += 2) {
     tile(std::integral_constant<int, 0>{}, kt);
