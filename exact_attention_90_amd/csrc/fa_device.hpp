@@ -150,6 +150,20 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char *base, int byte_off) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// s_waitcnt immediate that waits for at most n outstanding vector-memory operations and
+// leaves the other counters alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8)
+constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// ---- schedule pins ----------------------------------------------------------------
+// An empty asm that claims to rewrite x: the value must be computed before this point
+// and cannot be sunk past it, which keeps arithmetic in the pipeline step it was
+// written in (the scheduler fences keep the steps themselves in order).
+template <typename T>
+__device__ __forceinline__ void pin(T &x) {
+  asm volatile("" : "+v"(x));
+}
+
 // ---- workgroup order ----------------------------------------------------------------
 // Workgroups are handed to the 8 XCDs round-robin (id % 8).  Renumber them so that
 // consecutive logical ids - the Q tiles of one head, which read the same K/V -

@@ -32,29 +32,39 @@ namespace fa {
 // ====================================================================================
 // 16-bit inputs (binary16 or bfloat16), d in {64, 128}
 // ====================================================================================
-template <int D>
+template <int D, int WAVES>
 struct Cfg16 {
-  static constexpr int BM = kFusedBM;           // query rows per workgroup
+  static constexpr int NT = 64 * WAVES;         // threads per workgroup
+  static constexpr int BM = 32 * WAVES;         // query rows per workgroup (32 per wave)
   static constexpr int BN = 64;                 // keys per tile
   static constexpr int ROWB = D * 2;            // bytes per row
   static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
   static constexpr int TILEB = BN * ROWB;       // bytes of one K or V tile
-  static constexpr int CPT = TILEB / 16 / 256;  // chunks per thread per tile
-  static constexpr int QCPT = BM * CPR / 256;   // Q chunks per thread
+  static constexpr int CPT = TILEB / 16 / NT;   // chunks per thread per tile
+  static constexpr int QCPT = BM * CPR / NT;    // Q chunks per thread
   static constexpr int SB = BN / 32;            // 32-key S blocks per tile
   static constexpr int KC = D / 16;             // k-steps of the Q K product
   static constexpr int OB = D / 32;             // 32-wide blocks of the output
   static constexpr int PU = BN / 16;            // k-steps of the P V product
   static constexpr int LDS = 4 * TILEB;         // K and V, two stages each
-  static_assert(BM * ROWB <= 2 * TILEB, "Q staging must fit in the K stages");
+  static_assert(CPT >= 1 && TILEB % (16 * NT) == 0, "a tile is whole chunks per thread");
+  static_assert(BM * ROWB <= LDS, "Q staging must fit in the K and V stages");
+  // the rows a thread moves differ by NT / CPR per chunk, which must keep the swizzle
+  // keys (period 16 rows for 16-chunk rows, 16 for 8-chunk rows) unchanged
+  static_assert((NT / CPR) % 16 == 0, "thread row stride must preserve the swizzle key");
 };
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(256, 2) void fa_fwd16_kernel(
+template <int D, bool BF16, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int N,
     int nqt, int G, float c) {
-  using C = Cfg16<D>;
+  using C = Cfg16<D, WAVES>;
+  constexpr int SB = C::SB, OB = C::OB, PU = C::PU, CPT = C::CPT;
+  constexpr int NA = SB * C::KC;  // matrix-core steps of S^T = K Q^T per tile
+  constexpr int NB = OB * PU;     // matrix-core steps of O^T += V^T P^T per tile
+  constexpr int DK = 4;           // K operand reads kept in flight
+  constexpr int DV = 3;           // V operand reads (pairs) kept in flight
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *const Ks = smem;
   char *const Vs = smem + 2 * C::TILEB;
@@ -69,9 +79,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd16_kernel(
   const auto qrs = make_rsrc(Q + hoff, head_bytes);
   const auto krs = make_rsrc(K + hoff, head_bytes);
   const auto vrs = make_rsrc(V + hoff, head_bytes);
-  constexpr int ST_STEP = 256 * 16;  // bytes between a thread's chunks, in LDS and in memory
+  constexpr int ST_STEP = C::NT * 16;  // bytes between a thread's chunks, in LDS and memory
   // A tile of rows is one contiguous block of global memory: thread tid moves the
-  // 16-byte chunks tid + 256 i.  Their LDS rows differ by 256/CPR per i, which leaves
+  // 16-byte chunks tid + NT i.  Their LDS rows differ by NT/CPR per i, which leaves
   // the swizzle key unchanged, so one lane offset plus immediates addresses them all.
   const int srow = tid / C::CPR, sch = tid % C::CPR;
 
@@ -95,121 +105,287 @@ __global__ __launch_bounds__(256, 2) void fa_fwd16_kernel(
   // ---- per-lane LDS offsets, fixed for the whole loop ----
   const int st_k = srow * C::ROWB + swz_row<C::CPR>(srow, sch) * 16;
   const int st_v = srow * C::ROWB + swz_v<C::CPR>(srow, sch) * 16;
-  // K operand rows 32t + l32: the swizzle key depends on l32 only
-  int kofs[C::KC];
-#pragma unroll
-  for (int kc = 0; kc < C::KC; ++kc) kofs[kc] = l32 * C::ROWB + swz_row<C::CPR>(l32, 2 * kc + h) * 16;
+  // K operand rows 32t + l32 at logical chunk 2 kc + h: the XOR swizzle key k of row l32
+  // splits as chunk (2 kc + h) ^ k = 2 (kc ^ (k >> 1)) + (h ^ (k & 1)), so the byte offset
+  // is k_base + ((32 kc) ^ k_xor), one xor-add per k-step instead of KC live registers
+  int k_base, k_xor;
+  {
+    const int key = swz_row<C::CPR>(l32, 0);  // the key itself (chunk 0 ^ key)
+    k_base = l32 * C::ROWB + (h ^ (key & 1)) * 16;
+    k_xor = (key >> 1) * 32;
+  }
   // transposing V reads: lane j of 16-lane group G reads key row 16u + 8x + 4(G/2) + j/4
-  // at columns 32e + 16(G%2) + 4(j%4); the swizzle key depends on the lane only
-  const int grp = lane >> 4, j16 = lane & 15;
-  const int vrow0 = 4 * (grp >> 1) + (j16 >> 2);
-  const int vcol0 = 16 * (grp & 1) + 4 * (j16 & 3);
-  int vofs[C::OB];
-#pragma unroll
-  for (int e = 0; e < C::OB; ++e) {
-    const int col = 32 * e + vcol0;
-    vofs[e] = vrow0 * C::ROWB + swz_v<C::CPR>(vrow0, col >> 3) * 16 + (col & 7) * 2;
+  // at columns 32e + 16(G%2) + 4(j%4).  Column chunk 4e + c0 (c0 < 4) of row r sits at
+  // chunk (4e + c0) ^ 4 k(r) = 4 (e ^ k) + c0, so the byte offset is
+  // v_base + ((64 e) ^ v_xor) with lane constants v_base and v_xor
+  int v_base, v_xor;
+  {
+    const int grp = lane >> 4, j16 = lane & 15;
+    const int vrow0 = 4 * (grp >> 1) + (j16 >> 2);
+    const int vcol0 = 16 * (grp & 1) + 4 * (j16 & 3);
+    const int c0 = vcol0 >> 3;
+    v_base = vrow0 * C::ROWB + c0 * 16 + (vcol0 & 7) * 2;
+    v_xor = (swz_v<C::CPR>(vrow0, c0) ^ c0) * 16;  // 64 k(r): the swizzle's xor term
   }
 
   // ---- K/V tile movement ----
-  // K (and V for binary16 inputs) go from global memory straight into an LDS stage.
-  // LDS byte 16 c of a stage is written by lane c % 64 of wave (c / 64) % 4, instruction
-  // c / 256; that position holds logical chunk swz(row, c % CPR) of row c / CPR, and since
-  // each swizzle is an involution the lane's global offset within the tile is its st_k /
-  // st_v value.  bfloat16 V passes through registers so it can be widened to binary16.
+  // K and V tiles go from global memory straight into an LDS stage.  LDS byte 16 c of a
+  // stage is written by lane c % 64 of wave (c / 64) % WAVES, instruction c / NT; that
+  // position holds logical chunk swz(row, c % CPR) of row c / CPR, and since each swizzle
+  // is an involution the lane's global offset within the tile is its st_k / st_v value.
+  // Tiles past the end of the head read as zeros (buffer range check), so loads are
+  // issued unconditionally; their offsets stay below 2^31 for every accepted shape.
   const int dma_wave = __builtin_amdgcn_readfirstlane(w) * 1024;  // wave's 1 KiB of a step
-  [[maybe_unused]] u32x4 vreg[C::CPT];
-  auto fetch = [&](int kt, char *kb, char *vb) {
-    const int toff = kt * C::TILEB;
+  auto dma_k = [&](char *kb, int kt) {
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      buf_load16_lds(krs, kb + dma_wave + i * ST_STEP, st_k, toff + i * ST_STEP);
-      if constexpr (BF16)
-        vreg[i] = buf_load16(vrs, tid * 16, toff + i * ST_STEP);
-      else
-        buf_load16_lds(vrs, vb + dma_wave + i * ST_STEP, st_v, toff + i * ST_STEP);
-    }
+    for (int i = 0; i < CPT; ++i)
+      buf_load16_lds(krs, kb + dma_wave + i * ST_STEP, st_k, kt * C::TILEB + i * ST_STEP);
   };
-  auto stage = [&](char *vb) {
+  auto dma_v = [&](char *vb, int kt) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+      buf_load16_lds(vrs, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB + i * ST_STEP);
+  };
+  // bfloat16 V: the P V product runs in binary16, so each thread widens the chunks its
+  // own loads wrote (chunk i: 16 bytes at dma_wave + i ST_STEP + 16 lane), in place.
+  // Needs only this wave's loads to have landed; other waves read the stage after the
+  // barrier that ends the iteration.
+  auto widen_v = [&](char *vb, int i) {
     if constexpr (BF16) {
+      char *p = vb + dma_wave + i * ST_STEP;
+      u32x4 vv = lds_read16(p, lane * 16);
 #pragma unroll
-      for (int i = 0; i < C::CPT; ++i) {
-        // the P V product runs in binary16: widen V while staging
-        u32x4 vv = vreg[i];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) vv[q] = bf16x2_to_f16x2(vv[q]);
-        lds_write16(vb, st_v + i * ST_STEP, vv);
-      }
+      for (int q = 0; q < 4; ++q) vv[q] = bf16x2_to_f16x2(vv[q]);
+      lds_write16(p, lane * 16, vv);
     }
   };
+  // operand of matrix-core step i: S^T step i = (block t = i / KC, k-step i % KC);
+  // P V step i = (output block e = i % OB, key step u = i / OB).  kb / vb are the lane's
+  // base offsets into the K / V stage being read (stage offset + k_base / v_base).
+  auto k_op = [&](int kb, int i) {
+    const int t = i / C::KC, kc = i % C::KC;  // block-major: all k-steps of block 0 first
+    const int off = kb + ((32 * kc) ^ k_xor) + 32 * t * C::ROWB;
+    return lds_read16(smem, off);
+  };
+  auto v_op = [&](int vb, int i) {
+    const int u = i / OB, e = i % OB;
+    const int off = vb + ((64 * e) ^ v_xor);
+    const u32x2 a0 = lds_read_tr(smem, off + (16 * u) * C::ROWB);
+    const u32x2 a1 = lds_read_tr(smem, off + (16 * u + 8) * C::ROWB);
+    return u32x4{a0[0], a0[1], a1[0], a1[1]};
+  };
 
-  f32x16 o[C::OB];
+  f32x16 o[OB];
 #pragma unroll
-  for (int e = 0; e < C::OB; ++e) o[e] = f32x16{};
-  float mc = -INFINITY, l = 0.f;
-
+  for (int e = 0; e < OB; ++e) o[e] = f32x16{};
+  // online-softmax state of the lane's query row: running max (base-2 units), this
+  // lane's partial row sum, and, for the tile whose P is pending, its rescale factor
+  // alpha and P row sum
+  float mc = -INFINITY, l = 0.f, alpha = 0.f, rs = 0.f;
   const int nkt = (N + C::BN - 1) / C::BN;
+  const int nlast = N - (nkt - 1) * C::BN;  // valid keys of the last tile, 1 .. BN
 
-  // one key tile: BUF is the LDS stage holding it (compile-time, so every LDS address
-  // below is a lane register plus an immediate)
-  auto tile = [&](auto bufc, int kt) {
-    constexpr int BUF = decltype(bufc)::value;
-    const char *kb = Ks + BUF * C::TILEB;
-    const char *vb = Vs + BUF * C::TILEB;
-    const bool more = kt + 1 < nkt;
-    if (more) fetch(kt + 1, Ks + (BUF ^ 1) * C::TILEB, Vs + (BUF ^ 1) * C::TILEB);
-
-    // S^T = K Q^T: lane owns query row l32, keys 32t + 8(r/4) + 4h + r%4
-    f32x16 s[C::SB];
+  // ---- the softmax of one tile is split across the two halves of an iteration ----
+  // S^T holds 32 scores per lane: block 0 (keys 0-31 of the tile, registers s[0]) and
+  // block 1 (keys 32-63, s[1]); score x is s[x / 16][x % 16].
+  //   during B (the P V product of the previous tile): the row max over all 32 scores,
+  //     the new running max and alpha, then P = 2^(c s - c m) for block 0, which is packed
+  //     into operand blocks 0 and 1 as soon as the previous tile's P V steps release them
+  //   during A (the S product of the next tile, which rebuilds s[0] first and s[1] last):
+  //     P for block 1, packed into operand blocks 2 and 3 before s[1] is overwritten, the
+  //     row sum, l = alpha l + sum, and O = alpha O
+  // The row sum adds the 32 values of P in score order, as a single pass would.
+  constexpr int KC = C::KC;
+  constexpr int NMX = NB >= 16 ? 2 : 1;  // B steps of the row max
+  constexpr int NEB = NB - NMX - 1;      // B steps carrying block-0 exponentials
+  constexpr int NEA = KC - 1;            // A steps carrying block-1 exponentials
+  float mx = 0.f, sub = 0.f;
+  auto max_step = [&](f32x16 (&s)[SB], int k) {
+    const int b = k * 32 / NMX, e = (k + 1) * 32 / NMX;
+    if (k == 0) mx = s[0][0];
 #pragma unroll
-    for (int t = 0; t < C::SB; ++t) {
-      s[t] = f32x16{};
+    for (int x = 0; x < 32; ++x)
+      if (x >= b && x < e) mx = fmaxf(mx, s[x / 16][x % 16]);
+  };
+  auto finalize_max = [&]() {
+    mx = pair_max(mx);                       // full row max over the tile's keys
+    const float mc_new = fmaxf(mc, mx * c);  // running max in base-2 units
+    // a row that has seen only masked keys keeps alpha = 0 and P = 0 (no inf - inf)
+    alpha = (mc == -INFINITY) ? 0.f : ex2(mc - mc_new);
+    sub = (mc_new == -INFINITY) ? 0.f : mc_new;
+    mc = mc_new;
+    rs = 0.f;
+  };
+  auto exp_range = [&](f32x16 (&s)[SB], int b, int e) {
 #pragma unroll
-      for (int kc = 0; kc < C::KC; ++kc)
-        s[t] = mma16<BF16>(lds_read16(kb, kofs[kc] + 32 * t * C::ROWB), qf[kc], s[t]);
-    }
-
-    const int nvalid = N - kt * C::BN;
-    if (nvalid < C::BN)
-      softmax_tile<C::SB, C::OB, true>(s, o, mc, l, c, nvalid, h);
-    else
-      softmax_tile<C::SB, C::OB, false>(s, o, mc, l, c, nvalid, h);
-
-    // P -> binary16 operands: step u takes block u/2, registers 8(u%2) .. +7,
-    // i.e. keys 16u + 8x + 4h + s for slot 4x + s
-    u32x4 pf[C::PU];
-#pragma unroll
-    for (int u = 0; u < C::PU; ++u) {
-      const int t = u >> 1, rb = (u & 1) * 8;
-      pf[u] = u32x4{pack_f16(s[t][rb + 0], s[t][rb + 1]), pack_f16(s[t][rb + 2], s[t][rb + 3]),
-                    pack_f16(s[t][rb + 4], s[t][rb + 5]), pack_f16(s[t][rb + 6], s[t][rb + 7])};
-    }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int e = 0; e < C::OB; ++e)
-#pragma unroll
-      for (int u = 0; u < C::PU; ++u) {
-        u32x2 a0 = lds_read_tr(vb, vofs[e] + (16 * u) * C::ROWB);
-        u32x2 a1 = lds_read_tr(vb, vofs[e] + (16 * u + 8) * C::ROWB);
-        o[e] = mma_f16(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf[u], o[e]);
+    for (int x = 0; x < 32; ++x)
+      if (x >= b && x < e) {
+        const float p = ex2(fmaf(s[x / 16][x % 16], c, -sub));
+        s[x / 16][x % 16] = p;
+        rs += p;
       }
-
-    if (more) stage(Vs + (BUF ^ 1) * C::TILEB);
-    __syncthreads();  // also waits for this wave's loads into the other stage
+  };
+  // keys at or past nvalid of a tile are masked to -inf before its softmax
+  auto mask = [&](f32x16 (&s)[SB], int nvalid) {
+#pragma unroll
+    for (int t = 0; t < SB; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (key >= nvalid) s[t][r] = -INFINITY;
+      }
+  };
+  // P (fp32, S^T register layout) -> binary16 operands: step u takes block u/2,
+  // registers 8(u%2) .. +7, i.e. keys 16u + 8x + 4h + s for slot 4x + s
+  u32x4 pf[PU];
+  auto pack_u = [&](const f32x16 (&s)[SB], int u) {
+    const int t = u >> 1, rb = (u & 1) * 8;
+    pf[u] = u32x4{pack_f16(s[t][rb + 0], s[t][rb + 1]), pack_f16(s[t][rb + 2], s[t][rb + 3]),
+                  pack_f16(s[t][rb + 4], s[t][rb + 5]), pack_f16(s[t][rb + 6], s[t][rb + 7])};
+    pin(pf[u]);
+  };
+  // B step k's share of the softmax; operand block u (0 or 1) is packed at the first
+  // step where its 8 exponentials are done and its last reader (step OB u + OB - 1) of the
+  // previous tile's P V product has issued
+  auto b_exp_end = [](int k) { return k <= NMX ? 0 : (k - NMX) * 16 / NEB; };
+  auto b_pack_step = [&](int u) {
+    int k = NMX + 1;
+    while (b_exp_end(k) < 8 * u + 8) ++k;
+    return k > OB * u + OB ? k : OB * u + OB;
+  };
+  auto soft_b = [&](f32x16 (&s)[SB], int k) {
+    if (k < NMX) max_step(s, k);
+    else if (k == NMX) finalize_max();
+    else exp_range(s, b_exp_end(k - 1), b_exp_end(k));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (b_pack_step(u) == k) pack_u(s, u);
+  };
+  // A step k's share: block-1 exponentials on steps 0 .. NEA-1, then (step NEA) the last
+  // two operand blocks and l; O = alpha O on the steps that rebuild s[1]
+  auto soft_a = [&](f32x16 (&s)[SB], int k) {
+    if (k < NEA) exp_range(s, 16 + k * 16 / NEA, 16 + (k + 1) * 16 / NEA);
+    if (k == NEA) {
+      pack_u(s, 2);
+      pack_u(s, 3);
+      l = fmaf(l, alpha, rs);
+    }
+    if (k >= KC) {
+      constexpr int R = OB * 16 / KC;
+      const int q = k - KC;
+#pragma unroll
+      for (int x = 0; x < OB * 16; ++x)
+        if (x >= q * R && x < (q + 1) * R) o[x / 16][x % 16] *= alpha;
+      pin(o[q * R / 16]);
+    }
   };
 
-  fetch(0, Ks, Vs);
-  stage(Vs);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {
-    tile(std::integral_constant<int, 0>{}, kt);
-    if (kt + 1 < nkt) tile(std::integral_constant<int, 1>{}, kt + 1);
+  // S of the tile being started (becomes its P in place); the packed P of the tile
+  // whose P V product is pending lives in pf
+  f32x16 s[SB];
+  u32x4 kf[DK], vf[DV];
+  // S product step i, block-major so s[0] is rebuilt before s[1]
+  auto s_step = [&](int kb, int i, u32x4 kop) {
+    const int t = i / KC, kc = i % KC;
+    s[t] = mma16<BF16>(kop, qf[kc], kc == 0 ? f32x16{} : s[t]);
+  };
+
+  // ---- prologue: K_0, V_0 and K_1 staged; S_0 and the B share of its softmax ----
+  dma_v(Vs, 0);
+  dma_k(Ks, 0);
+  dma_k(Ks + C::TILEB, 1);
+  if constexpr (BF16) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) widen_v(Vs, i);
+  }
+  __syncthreads();  // also waits for this wave's loads into LDS
+#pragma unroll
+  for (int i = 0; i < NA; ++i) s_step(k_base, i, k_op(k_base, i));
+  if (nkt == 1 && nlast < C::BN) mask(s, nlast);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    soft_b(s, k);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __syncthreads();  // every wave is done with K_0 before stage 0 is refilled
+
+  // ---- steady state: iteration j (P = j % 2 selects the LDS stages) ----
+  //   A: K_{j+2} and V_{j+1} start towards LDS; S_{j+1} = K_{j+1} Q^T on the matrix
+  //      cores, while the VALU finishes the softmax of tile j and rescales O by alpha_j
+  //   B: O += V_j P_j on the matrix cores, while the VALU starts the softmax of S_{j+1}
+  //      and widens bfloat16 V_{j+1}
+  // The stages written in iteration j held K_j and V_{j-1}, last read in iteration j-1;
+  // the barrier that ends each iteration (and waits for the loads into LDS) orders every
+  // stage's last read before its next write and every write before its next read.
+  // MASKED: the tile started in this iteration (j + 1) is the last one, so its keys past
+  // N are masked; only the final iteration is compiled with it, keeping the mask out of
+  // the steady-state loop
+  auto iter = [&](int j, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const int P = j & 1;
+    // lane bases of this iteration's reads (the pins keep the offset arithmetic inside
+    // the loop rather than precomputed into live registers)
+    pin(k_xor);
+    pin(v_xor);
+    const int kb = k_base + (1 - P) * C::TILEB;         // K_{j+1}
+    const int vb = v_base + (2 + P) * C::TILEB;         // V_j
+    char *vw = Vs + (1 - P) * C::TILEB;                 // V_{j+1}
+    char *kw = Ks + P * C::TILEB;                       // K_{j+2}
+
+    // ---- A ----
+    dma_v(vw, j + 1);
+    dma_k(kw, j + 2);
+#pragma unroll
+    for (int i = 0; i < DK; ++i) kf[i] = k_op(kb, i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      s_step(kb, i, kf[i % DK]);
+      if (i + DK < NA) kf[i % DK] = k_op(kb, i + DK);
+      soft_a(s, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- B ----
+#pragma unroll
+    for (int i = 0; i < DV; ++i) vf[i] = v_op(vb, i);
+    if (MASKED && nlast < C::BN) mask(s, nlast);
+    // this wave's loads into LDS (issued at the start of A) have landed by now; the
+    // bfloat16 V they brought is widened in place during the P V product below
+    if constexpr (BF16) __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int u = i / OB, e = i % OB;
+      o[e] = mma_f16(vf[i % DV], pf[u], o[e]);
+      if (i + DV < NB) vf[i % DV] = v_op(vb, i + DV);
+      soft_b(s, i);
+      if (i % (NB / CPT) == NB / CPT - 1) widen_v(vw, i / (NB / CPT));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+  };
+
+  for (int j = 0; j + 2 < nkt; ++j) iter(j, std::false_type{});
+  if (nkt >= 2) iter(nkt - 2, std::true_type{});
+
+  // ---- last tile T = nkt - 1: the A share of its softmax, then its P V product ----
+  {
+    const int vb = v_base + (2 + ((nkt - 1) & 1)) * C::TILEB;
+#pragma unroll
+    for (int k = 0; k < NA; ++k) soft_a(s, k);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int u = i / OB, e = i % OB;
+      o[e] = mma_f16(v_op(vb, i), pf[u], o[e]);
+    }
   }
 
   const int row = q0 + 32 * w + l32;
-  store_rows<C::OB>(o, mc, l, O + hoff + int64_t(row) * D, LSE + int64_t(bh) * N + row, h,
-                    row < N);
+  store_rows<OB>(o, mc, l, O + hoff + int64_t(row) * D, LSE + int64_t(bh) * N + row, h,
+                 row < N);
 }
 
 // ====================================================================================
@@ -357,17 +533,23 @@ static hipError_t allow_lds(KernelT kernel, int bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int D, bool BF16>
+// Waves per workgroup of the 16-bit kernel: at d = 128, eight waves (256 query rows)
+// halve the K/V tile loads and the bfloat16 widening per query row; at d = 64 the
+// softmax dominates and four waves schedule better.
+template <int D>
+constexpr int waves16() { return D == 128 ? 8 : 4; }
+
+template <int D, bool BF16, int WAVES = waves16<D>()>
 static hipError_t run16(const Problem &p, hipStream_t stream) {
-  using C = Cfg16<D>;
-  auto kern = fa_fwd16_kernel<D, BF16>;
+  using C = Cfg16<D, WAVES>;
+  auto kern = fa_fwd16_kernel<D, BF16, WAVES>;
   // raise the dynamic-LDS cap once; a refusal surfaces as a launch error below
   static const hipError_t attr = allow_lds(kern, C::LDS);
   (void)attr;
   const int nqt = (p.N + C::BM - 1) / C::BM;
   const int G = nqt * p.B * p.H;
   const float c = p.scale * kLog2e;
-  hipLaunchKernelGGL(kern, dim3(G), dim3(256), C::LDS, stream,
+  hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
                      static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                      static_cast<const uint16_t *>(p.v), p.o, p.lse, p.N, nqt, G, c);
   return hipGetLastError();

@@ -18,7 +18,8 @@ struct Problem {
   int dtype;
 };
 
-// Query rows per workgroup of the fused kernel (every variant uses 4 waves x 32 rows).
+// Query rows per workgroup of the fused kernels: waves x 32 rows.  kFusedBM (4 waves) is
+// the smallest workgroup any fused kernel uses, so it bounds the grid of all of them.
 constexpr int kFusedBM = 128;
 // Largest grid (in workgroups) any launcher issues: 256 threads x 2^24 < 2^32 work-items.
 constexpr int64_t kMaxGrid = int64_t(1) << 24;
