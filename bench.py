@@ -129,6 +129,60 @@ def copy_calibration(mib: int, steps: int) -> int:
     return 0
 
 
+def short_sequence_study(reps: int) -> int:
+    """Where the fused kernel stops beating the three-kernel naive path: time per call
+    of both paths over a grid of short sequence lengths and head counts (inputs resident
+    on the device; events around `reps` back-to-back calls, so launch overhead counts as
+    it would for a caller).  One JSON line per point."""
+    import numpy as np
+    import torch
+
+    import exact_attention_90_amd as fa
+    from synth.inputs import make_qkv, to_torch
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    for dtype, d in (("bf16", 128), ("f16", 64)):
+        for B, H in ((1, 1), (1, 16), (8, 32)):
+            for N in (16, 32, 64, 128, 256, 512, 1024, 2048):
+                x = make_qkv(B, H, N, d, dtype, seed=7000 + N)
+                q, k, v = (to_torch(x[n], dtype).to(dev) for n in ("q", "k", "v"))
+                o = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
+                lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+                nb = fa.naive_workspace_bytes(B, H, N, q.dtype)
+                ws = (torch.empty(nb, dtype=torch.uint8, device=dev),
+                      torch.empty(nb, dtype=torch.uint8, device=dev))
+                scale32 = float(np.float32(1.0 / math.sqrt(d)))
+                calls = {
+                    "fused": lambda: fa.fwd(q, k, v, scale32, out=o, lse=lse),
+                    "naive": lambda: fa.naive_fwd(q, k, v, scale32, out=o, lse=lse, workspace=ws),
+                }
+                us = {}
+                for name, call in calls.items():
+                    for _ in range(10):
+                        call()
+                    torch.cuda.synchronize(dev)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(reps):
+                        call()
+                    e1.record(stream)
+                    torch.cuda.synchronize(dev)
+                    us[name] = e0.elapsed_time(e1) * 1e3 / reps
+                flops = 4.0 * B * H * N * N * d
+                print(json.dumps({
+                    "study": "short_sequence", "dtype": dtype, "B": B, "H": H, "N": N, "d": d,
+                    "fused_us": round(us["fused"], 2), "naive_us": round(us["naive"], 2),
+                    "naive_over_fused": round(us["naive"] / us["fused"], 2),
+                    "fused_tflops": round(flops / (us["fused"] * 1e-6) / 1e12, 3),
+                    "naive_tflops": round(flops / (us["naive"] * 1e-6) / 1e12, 3),
+                }), flush=True)
+                del ws, q, k, v, o, lse
+                torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,9 +197,14 @@ def main() -> int:
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run device-to-device copies of MIB MiB (a "
                          "plain copy of known size that scales the FETCH/WRITE counters)")
+    ap.add_argument("--short-seq-study", action="store_true",
+                    help="instead of one workload, time the fused and naive paths over short "
+                         "sequence lengths and head counts (one JSON line per point)")
     args = ap.parse_args()
     if args.copy_calibration:
         return copy_calibration(args.copy_calibration, max(1, args.steps))
+    if args.short_seq_study:
+        return short_sequence_study(reps=100)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -67,6 +67,16 @@ def test_tiny_and_ragged(N, dtype, d):
         assert err <= tol
 
 
+# key-tile counts 2, 3, 5, 8 and 10 (ragged and exact last tiles) and partial query
+# tiles of both workgroup sizes: every length of the software-pipelined loop, with the
+# masked iteration alone (2 tiles) and after odd and even numbers of steady iterations
+@pytest.mark.parametrize("N", [65, 191, 257, 449, 640])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+def test_pipeline_lengths(N, dtype, d):
+    m, _, _ = full_case(1, 2, N, d, dtype, seed=300 + N)
+    assert_parity(m, dtype, where=f"N={N} d={d} {dtype}")
+
+
 @pytest.mark.parametrize("dtype,mult", [("bf16", 3.0), ("f16", 8.0), ("bf16", 12.0)])
 def test_large_logits(dtype, mult):
     # logit standard deviation ~ mult^2: needs the running-max subtraction and rescale
