@@ -29,7 +29,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from synth.configs import WORKLOADS  # noqa: E402
+from synth.configs import HEADDIM_WORKLOADS, WORKLOADS  # noqa: E402
+
+ALL_WORKLOADS = {**WORKLOADS, **HEADDIM_WORKLOADS}
 
 METRIC = "fwd attention TFLOP/s & % of bf16 MFMA peak, B8 H32 N4096 d128"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # MI355X dense matrix-core peaks
@@ -188,7 +190,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="c3", choices=sorted(ALL_WORKLOADS))
     ap.add_argument("--shape", default=None, metavar="B,H,N,d,dtype",
                     help="measure an ad-hoc shape instead of a named workload (N(0,1) inputs)")
     ap.add_argument("--path", default="fused", choices=["fused", "naive"])
@@ -219,7 +221,7 @@ def main() -> int:
     import exact_attention_90_amd as fa
     from synth.inputs import make_qkv, to_torch
 
-    w = WORKLOADS[args.workload]
+    w = ALL_WORKLOADS[args.workload]
     if args.shape:
         from synth.configs import Workload
 

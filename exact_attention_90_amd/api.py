@@ -7,7 +7,7 @@ in the library's HIP kernels.  The function names follow the C boundary:
     naive_fwd(q, k, v, scale=None)  -> (o, lse)   materialised S/P contrast path
 
 q, k, v: contiguous [B, H, N, d] device tensors of one dtype (float32, float16 or
-bfloat16), d in {64, 128}.  o is float32 [B, H, N, d]; lse is float32 [B, H, N]
+bfloat16), d in {64, 128, 256}.  o is float32 [B, H, N, d]; lse is float32 [B, H, N]
 (natural log).  scale defaults to 1/sqrt(d).
 """
 from __future__ import annotations

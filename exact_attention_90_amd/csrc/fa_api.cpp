@@ -23,7 +23,7 @@ int check_args(const void *q, const void *k, const void *v, const float *o, cons
                int B, int H, int N, int d, float scale, int dtype, bool *empty) {
   *empty = false;
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEADDIM;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
   if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
   if (B == 0 || H == 0 || N == 0) {
@@ -118,7 +118,7 @@ const char *fa_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid or too large B, H or N";
-    case FA_ERR_HEADDIM: return "head dimension must be 64 or 128";
+    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";

@@ -95,6 +95,18 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   return pack_f16(lo, hi);
 }
 
+// sum of the eight binary16 values packed in v, added to acc in fp32 (each product by 1
+// is exact; v_dot2_f32_f16 accumulates in fp32)
+__device__ __forceinline__ float sum8_f16(u32x4 v, float acc) {
+  const f16x8 x = __builtin_bit_cast(f16x8, v);
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  acc = __builtin_amdgcn_fdot2(f16x2{x[0], x[1]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2(f16x2{x[2], x[3]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2(f16x2{x[4], x[5]}, one, acc, false);
+  acc = __builtin_amdgcn_fdot2(f16x2{x[6], x[7]}, one, acc, false);
+  return acc;
+}
+
 // ---- LDS swizzles (units: 16-byte chunks; cpr = chunks per row) -------------------
 // Row-operand tiles (Q, K) are read 16 bytes per lane with 16 lanes on 16
 // consecutive rows at the same logical chunk: spread those 16 rows over all banks.

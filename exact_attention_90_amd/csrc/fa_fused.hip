@@ -30,7 +30,7 @@
 namespace fa {
 
 // ====================================================================================
-// 16-bit inputs (binary16 or bfloat16), d in {64, 128}
+// 16-bit inputs (binary16 or bfloat16), d in {64, 128, 256}
 // ====================================================================================
 template <int D, int WAVES>
 struct Cfg16 {
@@ -47,15 +47,21 @@ struct Cfg16 {
   static constexpr int OB = D / 32;             // 32-wide blocks of the output
   static constexpr int PU = BN / 16;            // k-steps of the P V product
   static constexpr int LDS = 4 * TILEB;         // K and V, two stages each
+  // minimum waves per SIMD the registers must allow: at d = 256 one 32-row wave holds
+  // O (128 registers) and Q (64) and needs more than half of the register file
+  static constexpr int WPE = D == 256 ? 1 : 8 / WAVES;
   static_assert(CPT >= 1 && TILEB % (16 * NT) == 0, "a tile is whole chunks per thread");
   static_assert(BM * ROWB <= LDS, "Q staging must fit in the K and V stages");
-  // the rows a thread moves differ by NT / CPR per chunk, which must keep the swizzle
-  // keys (period 16 rows for 16-chunk rows, 16 for 8-chunk rows) unchanged
-  static_assert((NT / CPR) % 16 == 0, "thread row stride must preserve the swizzle key");
+  // the rows a thread moves differ by RSTEP per chunk.  The V swizzle key (period 4
+  // rows) never changes; the K/Q key (period 16 rows) changes only when RSTEP is an odd
+  // multiple of 8 (512-byte rows), and then alternates between two values
+  static constexpr int RSTEP = NT / CPR;
+  static constexpr bool KFLIP = RSTEP % 16 != 0;
+  static_assert(RSTEP % 8 == 0, "thread row stride must keep the swizzle keys periodic");
 };
 
 template <int D, bool BF16, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
+__global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES>::WPE)) void fa_fwd16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int N,
     int nqt, int G, float c) {
@@ -83,15 +89,17 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
   // A tile of rows is one contiguous block of global memory: thread tid moves the
   // 16-byte chunks tid + NT i.  Their LDS rows differ by NT/CPR per i, which leaves
   // the swizzle key unchanged, so one lane offset plus immediates addresses them all.
+  // With 512-byte rows the swizzle key of odd chunks is the other of two values.
   const int srow = tid / C::CPR, sch = tid % C::CPR;
+  const int st_k = srow * C::ROWB + swz_row<C::CPR>(srow, sch) * 16;
+  const int st_k1 =
+      C::KFLIP ? srow * C::ROWB + swz_row<C::CPR>(srow + C::RSTEP, sch) * 16 : st_k;
+  auto st_ki = [&](int i) { return (C::KFLIP && (i & 1)) ? st_k1 : st_k; };
 
   // ---- prologue: Q tile -> LDS (coalesced 16-byte loads) -> registers ----
-  {
-    const int st_q = srow * C::ROWB + swz_row<C::CPR>(srow, sch) * 16;
 #pragma unroll
-    for (int i = 0; i < C::QCPT; ++i)
-      lds_write16(Ks, st_q + i * ST_STEP, buf_load16(qrs, tid * 16, q0 * C::ROWB + i * ST_STEP));
-  }
+  for (int i = 0; i < C::QCPT; ++i)
+    lds_write16(Ks, st_ki(i) + i * ST_STEP, buf_load16(qrs, tid * 16, q0 * C::ROWB + i * ST_STEP));
   __syncthreads();
   u32x4 qf[C::KC];
   {
@@ -103,7 +111,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
   __syncthreads();
 
   // ---- per-lane LDS offsets, fixed for the whole loop ----
-  const int st_k = srow * C::ROWB + swz_row<C::CPR>(srow, sch) * 16;
   const int st_v = srow * C::ROWB + swz_v<C::CPR>(srow, sch) * 16;
   // K operand rows 32t + l32 at logical chunk 2 kc + h: the XOR swizzle key k of row l32
   // splits as chunk (2 kc + h) ^ k = 2 (kc ^ (k >> 1)) + (h ^ (k & 1)), so the byte offset
@@ -139,7 +146,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
   auto dma_k = [&](char *kb, int kt) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      buf_load16_lds(krs, kb + dma_wave + i * ST_STEP, st_k, kt * C::TILEB + i * ST_STEP);
+      buf_load16_lds(krs, kb + dma_wave + i * ST_STEP, st_ki(i), kt * C::TILEB + i * ST_STEP);
   };
   auto dma_v = [&](char *vb, int kt) {
 #pragma unroll
@@ -180,8 +187,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
   for (int e = 0; e < OB; ++e) o[e] = f32x16{};
   // online-softmax state of the lane's query row: running max (base-2 units), this
   // lane's partial row sum, and, for the tile whose P is pending, its rescale factor
-  // alpha and P row sum
-  float mc = -INFINITY, l = 0.f, alpha = 0.f, rs = 0.f;
+  // alpha and P row sum; lazy form only: the partial sums of P as rounded to binary16
+  // for the P V product (lp, and rp for the pending tile)
+  float mc = -INFINITY, l = 0.f, alpha = 0.f, rs = 0.f, lp = 0.f, rp = 0.f;
   const int nkt = (N + C::BN - 1) / C::BN;
   const int nlast = N - (nkt - 1) * C::BN;  // valid keys of the last tile, 1 .. BN
 
@@ -195,6 +203,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
   //     P for block 1, packed into operand blocks 2 and 3 before s[1] is overwritten, the
   //     row sum, l = alpha l + sum, and O = alpha O
   // The row sum adds the 32 values of P in score order, as a single pass would.
+  //
+  // At d = 256 the output accumulators live in the matrix-core (AGPR) registers, where a
+  // multiply costs a read, the multiply and a write per element.  There the reference
+  // max mc moves only when a tile's row max exceeds it by more than kTau (base-2 units):
+  // P <= 2^kTau stays far inside binary16 range, softmax is unchanged by the choice of
+  // reference, and most tiles leave every alpha at 1, so O is rescaled in a wave-uniform
+  // branch that is rarely taken.  P > 1 then carries the binary16 rounding of values
+  // that are not powers of two even for the row's largest score, so O is normalised by
+  // the sum of P as rounded for the P V product (the weights applied to V sum to one)
+  // and LSE by the exact sum.
+  constexpr bool LAZY = D == 256;
+  constexpr float kTau = 8.0f;
   constexpr int KC = C::KC;
   constexpr int NMX = NB >= 16 ? 2 : 1;  // B steps of the row max
   constexpr int NEB = NB - NMX - 1;      // B steps carrying block-0 exponentials
@@ -208,13 +228,17 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
       if (x >= b && x < e) mx = fmaxf(mx, s[x / 16][x % 16]);
   };
   auto finalize_max = [&]() {
-    mx = pair_max(mx);                       // full row max over the tile's keys
-    const float mc_new = fmaxf(mc, mx * c);  // running max in base-2 units
+    mx = pair_max(mx);  // full row max over the tile's keys
+    // running max in base-2 units (lazy: the reference, moved only past mc + kTau;
+    // -inf + kTau stays -inf, so the first tile with a valid key always sets it)
+    const float mxc = mx * c;
+    const float mc_new = LAZY ? (mxc > mc + kTau ? mxc : mc) : fmaxf(mc, mxc);
     // a row that has seen only masked keys keeps alpha = 0 and P = 0 (no inf - inf)
     alpha = (mc == -INFINITY) ? 0.f : ex2(mc - mc_new);
     sub = (mc_new == -INFINITY) ? 0.f : mc_new;
     mc = mc_new;
     rs = 0.f;
+    rp = 0.f;
   };
   auto exp_range = [&](f32x16 (&s)[SB], int b, int e) {
 #pragma unroll
@@ -243,6 +267,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
     pf[u] = u32x4{pack_f16(s[t][rb + 0], s[t][rb + 1]), pack_f16(s[t][rb + 2], s[t][rb + 3]),
                   pack_f16(s[t][rb + 4], s[t][rb + 5]), pack_f16(s[t][rb + 6], s[t][rb + 7])};
     pin(pf[u]);
+    if constexpr (LAZY) rp = sum8_f16(pf[u], rp);
   };
   // B step k's share of the softmax; operand block u (0 or 1) is packed at the first
   // step where its 8 exponentials are done and its last reader (step OB u + OB - 1) of the
@@ -269,14 +294,27 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
       pack_u(s, 2);
       pack_u(s, 3);
       l = fmaf(l, alpha, rs);
+      if constexpr (LAZY) lp = fmaf(lp, alpha, rp);
     }
-    if (k >= KC) {
+    if (!LAZY && k >= KC) {
       constexpr int R = OB * 16 / KC;
       const int q = k - KC;
 #pragma unroll
       for (int x = 0; x < OB * 16; ++x)
         if (x >= q * R && x < (q + 1) * R) o[x / 16][x % 16] *= alpha;
       pin(o[q * R / 16]);
+    }
+  };
+
+  // lazy form: O = alpha O for the whole tile, skipped when every alpha of the wave is 1
+  auto rescale_lazy = [&]() __attribute__((always_inline)) {
+    if constexpr (LAZY) {
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int e = 0; e < OB; ++e)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[e][r] *= alpha;
+      }
     }
   };
 
@@ -337,6 +375,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
     // ---- A ----
     dma_v(vw, j + 1);
     dma_k(kw, j + 2);
+    rescale_lazy();
 #pragma unroll
     for (int i = 0; i < DK; ++i) kf[i] = k_op(kb, i);
     __builtin_amdgcn_sched_barrier(0);
@@ -374,6 +413,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
   // ---- last tile T = nkt - 1: the A share of its softmax, then its P V product ----
   {
     const int vb = v_base + (2 + ((nkt - 1) & 1)) * C::TILEB;
+    rescale_lazy();
 #pragma unroll
     for (int k = 0; k < NA; ++k) soft_a(s, k);
 #pragma unroll
@@ -384,17 +424,17 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void fa_fwd16_kernel(
   }
 
   const int row = q0 + 32 * w + l32;
-  store_rows<OB>(o, mc, l, O + hoff + int64_t(row) * D, LSE + int64_t(bh) * N + row, h,
-                 row < N);
+  store_rows<OB>(o, mc, l, LAZY ? lp : l, O + hoff + int64_t(row) * D,
+                 LSE + int64_t(bh) * N + row, h, row < N);
 }
 
 // ====================================================================================
-// fp32 inputs, d in {64, 128}: fp32 matrix cores, fp32 P
+// fp32 inputs, d in {64, 128, 256}: fp32 matrix cores, fp32 P
 // ====================================================================================
 template <int D>
 struct Cfg32 {
   static constexpr int BM = kFusedBM;
-  static constexpr int BN = 64;
+  static constexpr int BN = D == 256 ? 32 : 64;  // two K and two V stages fit in LDS
   static constexpr int ROWB = D * 4;
   static constexpr int CPR = ROWB / 16;
   static constexpr int TILEB = BN * ROWB;
@@ -404,7 +444,10 @@ struct Cfg32 {
   static constexpr int KC = D / 8;  // 16-byte chunks per lane half: 4 k-steps each
   static constexpr int OB = D / 32;
   static constexpr int LDS = 4 * TILEB;
-  static_assert(BM * ROWB <= 2 * TILEB, "Q staging must fit in the K stages");
+  static_assert(BM * ROWB <= LDS, "Q staging must fit in the K and V stages");
+  // at d = 256, Q and O fill the registers: fence the unrolled loops so that the LDS
+  // operand reads are not hoisted far ahead of their products
+  static constexpr bool FENCE = D == 256;
 };
 
 template <int D>
@@ -470,6 +513,9 @@ __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
   for (int e = 0; e < C::OB; ++e) o[e] = f32x16{};
   float mc = -INFINITY, l = 0.f;
 
+  // the next tile's loads are issued before the current tile's compute; at d = 256 the
+  // registers that would hold them in flight are not there, so they follow it
+  constexpr bool PREFETCH = D <= 128;
   const int nkt = (N + C::BN - 1) / C::BN;
   fetch(0);
   stage(0);
@@ -479,19 +525,27 @@ __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
     const int buf = kt & 1;
     const char *kb = Ks + buf * C::TILEB;
     const char *vb = Vs + buf * C::TILEB;
-    if (kt + 1 < nkt) fetch(kt + 1);
+    if (PREFETCH && kt + 1 < nkt) fetch(kt + 1);
 
+    // at d = 256, lane ids re-pinned per tile keep the operand offsets computed next to
+    // their use instead of hoisted out of the loop into registers
+    int lx = l32, hx = h;
+    if constexpr (C::FENCE) {
+      pin(lx);
+      pin(hx);
+    }
     f32x16 s[C::SB];
 #pragma unroll
     for (int t = 0; t < C::SB; ++t) {
       s[t] = f32x16{};
-      const int kr = 32 * t + l32;
+      const int kr = 32 * t + lx;
 #pragma unroll
       for (int kc = 0; kc < C::KC; ++kc) {
         f32x4 kf = __builtin_bit_cast(
-            f32x4, lds_read16(kb, kr * C::ROWB + swz_row<C::CPR>(kr, 2 * kc + h) * 16));
+            f32x4, lds_read16(kb, kr * C::ROWB + swz_row<C::CPR>(kr, 2 * kc + hx) * 16));
 #pragma unroll
         for (int i = 0; i < 4; ++i) s[t] = mma_f32(kf[i], qf[kc][i], s[t]);
+        if constexpr (C::FENCE) __builtin_amdgcn_sched_barrier(0);
       }
     }
 
@@ -505,24 +559,29 @@ __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
     // h, key 32t + 8(r/4) + 4h + r%4; the V operand is that key's row, column 32e + l32
 #pragma unroll
     for (int e = 0; e < C::OB; ++e) {
-      const int col = 32 * e + l32, ch = col >> 2, cb = (col & 3) * 4;
+      const int col = 32 * e + lx, ch = col >> 2, cb = (col & 3) * 4;
 #pragma unroll
       for (int t = 0; t < C::SB; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int key = 32 * t + 8 * (r >> 2) + 4 * hx + (r & 3);
           const float vv =
               *reinterpret_cast<const float *>(vb + key * C::ROWB + swz_row<C::CPR>(key, ch) * 16 + cb);
           o[e] = mma_f32(vv, s[t][r], o[e]);
+          if constexpr (C::FENCE)
+            if (r % 4 == 3) __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    if (kt + 1 < nkt) stage(buf ^ 1);
+    if (kt + 1 < nkt) {
+      if (!PREFETCH) fetch(kt + 1);
+      stage(buf ^ 1);
+    }
     __syncthreads();
   }
 
   const int row = q0 + 32 * w + l32;
-  store_rows<C::OB>(o, mc, l, O + hoff + int64_t(row) * D, LSE + int64_t(bh) * N + row, h,
+  store_rows<C::OB>(o, mc, l, l, O + hoff + int64_t(row) * D, LSE + int64_t(bh) * N + row, h,
                     row < N);
 }
 
@@ -535,7 +594,8 @@ static hipError_t allow_lds(KernelT kernel, int bytes) {
 
 // Waves per workgroup of the 16-bit kernel: at d = 128, eight waves (256 query rows)
 // halve the K/V tile loads and the bfloat16 widening per query row; at d = 64 the
-// softmax dominates and four waves schedule better.
+// softmax dominates and four waves schedule better; at d = 256 a wave needs more than
+// half a SIMD's registers, so four waves (one per SIMD) are all a compute unit holds.
 template <int D>
 constexpr int waves16() { return D == 128 ? 8 : 4; }
 
@@ -573,9 +633,18 @@ static hipError_t run32(const Problem &p, hipStream_t stream) {
 
 hipError_t launch_fused(const Problem &p, hipStream_t stream) {
   switch (p.dtype) {
-    case kF16: return p.d == 128 ? run16<128, false>(p, stream) : run16<64, false>(p, stream);
-    case kBF16: return p.d == 128 ? run16<128, true>(p, stream) : run16<64, true>(p, stream);
-    default: return p.d == 128 ? run32<128>(p, stream) : run32<64>(p, stream);
+    case kF16:
+      return p.d == 256 ? run16<256, false>(p, stream)
+             : p.d == 128 ? run16<128, false>(p, stream)
+                          : run16<64, false>(p, stream);
+    case kBF16:
+      return p.d == 256 ? run16<256, true>(p, stream)
+             : p.d == 128 ? run16<128, true>(p, stream)
+                          : run16<64, true>(p, stream);
+    default:
+      return p.d == 256 ? run32<256>(p, stream)
+             : p.d == 128 ? run32<128>(p, stream)
+                          : run32<64>(p, stream);
   }
 }
 

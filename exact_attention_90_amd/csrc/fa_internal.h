@@ -1,6 +1,6 @@
 // Internal launch interface between the C boundary (fa_api.cpp) and the kernels.
 // Every launcher assumes its arguments were validated by the boundary: shapes
-// positive, d in {64, 128}, pointers non-null and aligned, grid within limits.
+// positive, d in {64, 128, 256}, pointers non-null and aligned, grid within limits.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -254,14 +254,17 @@ static hipError_t run_naive(const Problem &p, void *s_ws, void *p_ws, hipStream_
 hipError_t launch_naive(const Problem &p, void *s_ws, void *p_ws, hipStream_t stream) {
   switch (p.dtype) {
     case kF16:
-      return p.d == 128 ? run_naive<kF16, 128>(p, s_ws, p_ws, stream)
-                        : run_naive<kF16, 64>(p, s_ws, p_ws, stream);
+      return p.d == 256   ? run_naive<kF16, 256>(p, s_ws, p_ws, stream)
+             : p.d == 128 ? run_naive<kF16, 128>(p, s_ws, p_ws, stream)
+                          : run_naive<kF16, 64>(p, s_ws, p_ws, stream);
     case kBF16:
-      return p.d == 128 ? run_naive<kBF16, 128>(p, s_ws, p_ws, stream)
-                        : run_naive<kBF16, 64>(p, s_ws, p_ws, stream);
+      return p.d == 256   ? run_naive<kBF16, 256>(p, s_ws, p_ws, stream)
+             : p.d == 128 ? run_naive<kBF16, 128>(p, s_ws, p_ws, stream)
+                          : run_naive<kBF16, 64>(p, s_ws, p_ws, stream);
     default:
-      return p.d == 128 ? run_naive<kF32, 128>(p, s_ws, p_ws, stream)
-                        : run_naive<kF32, 64>(p, s_ws, p_ws, stream);
+      return p.d == 256   ? run_naive<kF32, 256>(p, s_ws, p_ws, stream)
+             : p.d == 128 ? run_naive<kF32, 128>(p, s_ws, p_ws, stream)
+                          : run_naive<kF32, 64>(p, s_ws, p_ws, stream);
   }
 }
 

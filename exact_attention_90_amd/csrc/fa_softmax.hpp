@@ -69,12 +69,14 @@ __device__ __forceinline__ void pack_p(const f32x16 (&s)[SB], u32x4 (&pf)[2 * SB
                   pack_f16(s[t][rb + 4], s[t][rb + 5]), pack_f16(s[t][rb + 6], s[t][rb + 7])};
   }
 }
-// Epilogue: O / l and LSE for the lane's query row.
+// Epilogue: O / lnorm and LSE = (mc + log2 l) ln 2 for the lane's query row.  lnorm is
+// the row sum O is normalised by: l itself, or the sum of P as rounded for the P V
+// product, which makes the weights applied to V sum to exactly one.
 template <int OB>
-__device__ __forceinline__ void store_rows(f32x16 (&o)[OB], float mc, float l, float *orow,
-                                           float *lse, int h, bool valid) {
+__device__ __forceinline__ void store_rows(f32x16 (&o)[OB], float mc, float l, float lnorm,
+                                           float *orow, float *lse, int h, bool valid) {
   const float lt = pair_sum(l);  // both halves of the row hold partial sums
-  const float inv = 1.0f / lt;
+  const float inv = 1.0f / pair_sum(lnorm);
   if (!valid) return;
 #pragma unroll
   for (int e = 0; e < OB; ++e)

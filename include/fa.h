@@ -53,7 +53,7 @@ enum fa_status {
     FA_ERR_NULL = 1,      /* a required pointer is NULL (and the problem is not empty) */
     FA_ERR_SHAPE = 2,     /* B, H or N negative, or too large: B*H*ceil(N/128) > 2^24
                              workgroups, or one head's N*d*elem > 2^31 - 2^17 bytes */
-    FA_ERR_HEADDIM = 3,   /* d is not 64 or 128 */
+    FA_ERR_HEADDIM = 3,   /* d is not 64, 128 or 256 */
     FA_ERR_DTYPE = 4,     /* dtype is not one of fa_dtype */
     FA_ERR_SCALE = 5,     /* scale is not a finite number > 0 */
     FA_ERR_ALIGN = 6,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
@@ -74,7 +74,7 @@ enum fa_status {
  *            N need not be a multiple of any tile size.  If B*H*N == 0 the call
  *            checks its other arguments and returns FA_OK without launching
  *            (pointers may then be NULL).
- *   d        head dimension: 64 or 128.
+ *   d        head dimension: 64, 128 or 256 (every dtype).
  *   scale    softmax scale, finite and > 0 (usually 1/sqrt(d)).  It multiplies
  *            the float32 dot products; it is never folded into 16-bit inputs.
  *   dtype    FA_F32, FA_F16 or FA_BF16.

@@ -56,3 +56,9 @@ PAGE_WORKLOADS = {
     # N = 64, d = 64 smallest element-wise debug size recommended by the tutorial
     "p_n64_d64": Workload("p_n64_d64", 1, 2, 64, 64, "f16", 1.0, 12, "tutorial N=64 D=64 debug size"),
 }
+
+# Head-size variant of the headline shape: d = 256 with the same B*H*N^2*d (equal flops
+# and equal tensor bytes), so its throughput compares directly with c3.
+HEADDIM_WORKLOADS = {
+    "d256": Workload("d256", 4, 32, 4096, 256, "bf16", 1.0, 6, "bf16 d256, c3's flops and bytes"),
+}

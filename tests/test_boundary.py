@@ -77,7 +77,7 @@ def call(lib, q=A, k=B_, v=C_, o=O_, lse=L_, B=1, H=1, N=128, d=64, scale=0.125,
 
 @pytest.mark.parametrize("kwargs,code", [
     (dict(dtype=3), 4), (dict(dtype=-1), 4),
-    (dict(d=96), 3), (dict(d=0), 3), (dict(d=256), 3),
+    (dict(d=96), 3), (dict(d=0), 3), (dict(d=192), 3), (dict(d=512), 3),
     (dict(scale=0.0), 5), (dict(scale=-0.1), 5), (dict(scale=math.inf), 5), (dict(scale=math.nan), 5),
     (dict(B=-1), 2), (dict(H=-2), 2), (dict(N=-5), 2),
     (dict(q=None), 1), (dict(v=None), 1), (dict(lse=None), 1),
@@ -85,6 +85,8 @@ def call(lib, q=A, k=B_, v=C_, o=O_, lse=L_, B=1, H=1, N=128, d=64, scale=0.125,
     (dict(B=2**20, H=2**10, N=2**12), 2),                    # grid beyond 2^24 workgroups
     (dict(B=2**16, H=2**16, N=1), 2),                        # B*H beyond int
     (dict(N=2**23, d=128, dtype=1), 2),                      # one head beyond 2^31 bytes
+    (dict(N=2**22, d=256, dtype=2), 2),
+    (dict(N=2**21, d=256, dtype=0), 2),
 ])
 def test_fwd_rejects_bad_arguments_before_any_device_call(lib, kwargs, code):
     assert call(lib, **kwargs) == code
