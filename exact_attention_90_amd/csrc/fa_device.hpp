@@ -143,12 +143,33 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
 
 // 16 bytes per lane from global memory straight into LDS, without passing through
 // registers: lane l of the wave writes lds_wave_base + 16 l (lds_wave_base is uniform
-// across the wave).  Out-of-range dwords are written as zeros.  Completion is counted
-// by vmcnt like any other global load.
+// across the wave; m0 carries it, and one wait state separates its write from the load).
+// Out-of-range dwords are written as zeros.  Completion is counted by vmcnt like any
+// other global load, in issue order.
+//
+// The load is issued as inline assembly, which the compiler's wait-count tracking does
+// not see.  For the builtin form the compiler cannot tell which LDS stage a later
+// transposing read addresses, so it waits for every load into LDS in flight before each
+// such read, including loads of stages read only in later iterations.  Here the caller
+// waits explicitly (s_waitcnt vmcnt) for exactly the loads a barrier publishes.  The
+// compiler's own waits for the loads it tracks stay correct: loads retire in order, so
+// extra untracked loads can only make those waits longer.
 __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char *lds_wave_base,
                                                int voff, int soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void *)lds_wave_base, 16, voff, soff, 0, 0);
+  const uint32_t m0v =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_wave_base;
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :
+               : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0v)
+               : "memory");
+}
+
+// Workgroup barrier that orders LDS accesses only: the loads into LDS above are not
+// waited for here (the caller's s_waitcnt vmcnt decides which must have landed).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ u32x4 lds_read16(const char *base, int byte_off) {

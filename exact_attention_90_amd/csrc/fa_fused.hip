@@ -328,16 +328,25 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES>::WPE)) void fa_fwd16_k
     s[t] = mma16<BF16>(kop, qf[kc], kc == 0 ? f32x16{} : s[t]);
   };
 
+  // Loads into LDS are waited for explicitly: each wave waits (s_waitcnt vmcnt, loads
+  // retire in issue order) for its own loads of the stages the next barrier publishes,
+  // and leaves the younger ones in flight.
+  auto wait_loads = [](auto n) {  // at most n.value of this wave's loads in flight
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(decltype(n)::value));
+  };
+  using in_flight_0 = std::integral_constant<int, 0>;
+  using in_flight_1 = std::integral_constant<int, CPT>;  // one tile of K or V
+
   // ---- prologue: K_0, V_0 and K_1 staged; S_0 and the B share of its softmax ----
-  dma_v(Vs, 0);
   dma_k(Ks, 0);
+  dma_v(Vs, 0);
   dma_k(Ks + C::TILEB, 1);
+  wait_loads(in_flight_1{});  // K_0 and V_0 have landed
   if constexpr (BF16) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
 #pragma unroll
     for (int i = 0; i < CPT; ++i) widen_v(Vs, i);
   }
-  __syncthreads();  // also waits for this wave's loads into LDS
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < NA; ++i) s_step(k_base, i, k_op(k_base, i));
   if (nkt == 1 && nlast < C::BN) mask(s, nlast);
@@ -347,16 +356,21 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES>::WPE)) void fa_fwd16_k
     soft_b(s, k);
     __builtin_amdgcn_sched_barrier(0);
   }
-  __syncthreads();  // every wave is done with K_0 before stage 0 is refilled
+  // K_1 has landed, and every wave is done with K_0 before stage 0 is refilled
+  wait_loads(in_flight_0{});
+  lds_barrier();
 
   // ---- steady state: iteration j (P = j % 2 selects the LDS stages) ----
-  //   A: K_{j+2} and V_{j+1} start towards LDS; S_{j+1} = K_{j+1} Q^T on the matrix
+  //   A: V_{j+1} and K_{j+2} start towards LDS; S_{j+1} = K_{j+1} Q^T on the matrix
   //      cores, while the VALU finishes the softmax of tile j and rescales O by alpha_j
   //   B: O += V_j P_j on the matrix cores, while the VALU starts the softmax of S_{j+1}
   //      and widens bfloat16 V_{j+1}
   // The stages written in iteration j held K_j and V_{j-1}, last read in iteration j-1;
-  // the barrier that ends each iteration (and waits for the loads into LDS) orders every
-  // stage's last read before its next write and every write before its next read.
+  // the barrier that ends each iteration orders every stage's last read before its next
+  // write, and every write before its next read: before it each wave waits for its loads
+  // of V_{j+1} and K_{j+2}, which iteration j + 1 reads.  B waits for V_{j+1} alone (it
+  // was issued first) before widening it, and the transposing reads of V_j wait for
+  // nothing.
   // MASKED: the tile started in this iteration (j + 1) is the last one, so its keys past
   // N are masked; only the final iteration is compiled with it, keeping the mask out of
   // the steady-state loop
@@ -369,7 +383,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES>::WPE)) void fa_fwd16_k
     pin(v_xor);
     const int kb = k_base + (1 - P) * C::TILEB;         // K_{j+1}
     const int vb = v_base + (2 + P) * C::TILEB;         // V_j
-    char *vw = Vs + (1 - P) * C::TILEB;                 // V_{j+1}
+    char *vw = Vs + (1 - P) * C::TILEB;                 // V_{j+1}, widened in B
     char *kw = Ks + P * C::TILEB;                       // K_{j+2}
 
     // ---- A ----
@@ -391,9 +405,9 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES>::WPE)) void fa_fwd16_k
 #pragma unroll
     for (int i = 0; i < DV; ++i) vf[i] = v_op(vb, i);
     if (MASKED && nlast < C::BN) mask(s, nlast);
-    // this wave's loads into LDS (issued at the start of A) have landed by now; the
-    // bfloat16 V they brought is widened in place during the P V product below
-    if constexpr (BF16) __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    // bfloat16 V_{j+1} is widened in place during the P V product below, once this
+    // wave's loads of it have landed (the loads issued after it may stay in flight)
+    if constexpr (BF16) wait_loads(in_flight_1{});
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -404,7 +418,8 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES>::WPE)) void fa_fwd16_k
       if (i % (NB / CPT) == NB / CPT - 1) widen_v(vw, i / (NB / CPT));
       __builtin_amdgcn_sched_barrier(0);
     }
-    __syncthreads();
+    wait_loads(in_flight_0{});
+    lds_barrier();
   };
 
   for (int j = 0; j + 2 < nkt; ++j) iter(j, std::false_type{});
@@ -423,9 +438,14 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES>::WPE)) void fa_fwd16_k
     }
   }
 
-  const int row = q0 + 32 * w + l32;
-  store_rows<OB>(o, mc, l, LAZY ? lp : l, O + hoff + int64_t(row) * D,
-                 LSE + int64_t(bh) * N + row, h, row < N);
+  // every wave is done with the K/V stages before they hold the output
+  lds_barrier();
+  constexpr int WAVE_LDS = C::LDS / WAVES;                 // bytes of a wave's region
+  constexpr int NHALF = (32 * D * 4 + WAVE_LDS - 1) / WAVE_LDS;
+  const int row0 = q0 + 32 * w;  // the wave's first query row
+  store_rows_lds<D, NHALF>(o, mc, l, LAZY ? lp : l, smem + w * WAVE_LDS,
+                           O + hoff + int64_t(row0) * D, LSE + int64_t(bh) * N + row0, lane,
+                           N - row0);
 }
 
 // ====================================================================================

@@ -89,4 +89,50 @@ __device__ __forceinline__ void store_rows(f32x16 (&o)[OB], float mc, float l, f
   if (h == 0) *lse = (mc + lg2(lt)) * kLn2;
 }
 
+// Epilogue through LDS for a wave's 32 query rows.  Written straight from the matrix-core
+// layout, one store instruction covers 32 B of each of 32 rows, and those partial lines
+// reach memory separately (up to 2.5x the bytes of O at d = 256).  Here the wave first
+// writes O / lnorm to its own LDS region (wave_lds, 32 x D / NHALF floats, no other
+// wave touches it), then reads it back row-contiguous so that every store instruction
+// writes whole rows of O (whole 128-byte lines).  NHALF > 1 stages the columns in
+// parts when the region holds only part of a row.  nvalid = rows of this wave that
+// exist (rows >= nvalid are not written).  Within one wave LDS accesses complete in
+// order, so no barrier is needed between the write, the read and the next part.
+template <int D, int NHALF>
+__device__ __forceinline__ void store_rows_lds(f32x16 (&o)[D / 32], float mc, float l,
+                                               float lnorm, char *wave_lds, float *orow0,
+                                               float *lse0, int lane, int nvalid) {
+  constexpr int OB = D / 32;
+  constexpr int EPH = OB / NHALF;        // 32-column blocks per part
+  constexpr int CH = EPH * 8;            // 16-byte chunks of a row per part
+  constexpr int RPI = 64 / CH;           // rows per read-back instruction
+  static_assert(CH % 16 == 0 && 64 % CH == 0, "row parts of 16..64 chunks");
+  const int h = lane >> 5, l32 = lane & 31;
+  const float lt = pair_sum(l);  // both halves of the row hold partial sums
+  const float inv = 1.0f / pair_sum(lnorm);
+  if (h == 0 && l32 < nvalid) lse0[l32] = (mc + lg2(lt)) * kLn2;
+  // chunk c of row r sits at chunk c ^ (r % 16) of the row: the 8 rows a write phase
+  // covers land on distinct banks, and a read of whole rows is a permutation
+#pragma unroll
+  for (int k = 0; k < NHALF; ++k) {
+#pragma unroll
+    for (int e = k * EPH; e < (k + 1) * EPH; ++e)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = 8 * (e - k * EPH) + 2 * g + h;  // columns 32e + 8g + 4h .. +3
+        f32x4 v = {o[e][4 * g] * inv, o[e][4 * g + 1] * inv, o[e][4 * g + 2] * inv,
+                   o[e][4 * g + 3] * inv};
+        *reinterpret_cast<f32x4 *>(wave_lds + (l32 * CH + (c ^ (l32 & 15))) * 16) = v;
+      }
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + lane / CH, c = lane % CH;
+      const f32x4 v =
+          *reinterpret_cast<const f32x4 *>(wave_lds + (r * CH + (c ^ (r & 15))) * 16);
+      if (r < nvalid)
+        *reinterpret_cast<f32x4 *>(orow0 + int64_t(r) * D + k * (CH * 4) + c * 4) = v;
+    }
+  }
+}
+
 }  // namespace fa
