@@ -12,6 +12,10 @@ the row max subtracted, o = P V, and LSE = m + ln(sum exp(s - m)).
 ``online_head`` runs the blockwise online-softmax recurrences of the MUSA guide's
 FlashAttention formula (steps 1-4, a-f) and records (m, l) after every block.
 
+``attention_bwd`` gives dQ, dK, dV for an upstream gradient dO: the chain rule of
+O = softmax(scale Q K^T) V with P recomputed (Triton tutorial, sections 2.4 and 4.4),
+written out in the C source.
+
 Inputs are storage bits as produced by ``synth.inputs`` (float32 arrays, or uint16
 bit patterns for f16/bf16); they are widened exactly to double inside the C code.
 """
@@ -51,7 +55,10 @@ def _configure(lib):
                                       ctypes.c_double, I64, P, P, P, P]
     lib.oracle_online_head.argtypes = [P, P, P, ctypes.c_int, I64, I64, I64, I64,
                                        ctypes.c_double, I64, I64, P, P, P, P]
-    for f in (lib.oracle_attention, lib.oracle_head_steps, lib.oracle_online_head):
+    lib.oracle_attention_bwd.argtypes = [P, P, P, P, ctypes.c_int, I64, I64, I64, I64,
+                                         ctypes.c_double, P, I64, P, P, P]
+    for f in (lib.oracle_attention, lib.oracle_head_steps, lib.oracle_online_head,
+              lib.oracle_attention_bwd):
         f.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -166,3 +173,26 @@ def online_head(q, k, v, dtype: str, scale: float, block: int, head: int = 0):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def attention_bwd(q, k, v, dout, dtype: str, scale: float, heads=None):
+    """Oracle gradients (dq, dk, dv) of O with respect to Q, K, V for the upstream
+    gradient dout (float32 [B, H, N, d]).  heads: None for every head (outputs
+    [B, H, N, d]) or ascending head indices b*H + h (outputs [len(heads), N, d])."""
+    q, k, v = _prep(q, k, v, dtype)
+    dout = np.ascontiguousarray(dout, dtype=np.float32)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have the [B, H, N, d] shape of q")
+    B, H, N, d = q.shape
+    lib = _load()
+    if heads is None:
+        shape, hp, nh = (B, H, N, d), None, B * H
+    else:
+        hs = np.ascontiguousarray(np.asarray(heads, dtype=np.int64).ravel())
+        shape, hp, nh = (len(hs), N, d), _ptr(hs), len(hs)
+    dq, dk, dv = (np.empty(shape, np.float64) for _ in range(3))
+    rc = lib.oracle_attention_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _CODES[dtype], B, H, N,
+                                  d, float(scale), hp, nh, _ptr(dq), _ptr(dk), _ptr(dv))
+    if rc:
+        raise RuntimeError(f"oracle_attention_bwd failed ({rc})")
+    return dq, dk, dv

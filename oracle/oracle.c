@@ -24,6 +24,9 @@
  * after every key block.  Tests use it only to show that the recurrences reach
  * the three-step result.
  *
+ * A third entry point, oracle_attention_bwd, gives the gradients of O with respect
+ * to Q, K and V (the backward pass, by the chain rule; see its comment).
+ *
  * Inputs are the storage bits the GPU receives (fp32, IEEE binary16 or
  * bfloat16), widened exactly to double.  All arithmetic is double.
  * Parity pins: see tests/test_oracle.py (brute force, closed forms, library
@@ -336,6 +339,102 @@ int oracle_online_head(const void *q, const void *k, const void *v, int dtype, i
     free(Vd);
     free(sblk);
     return 0;
+}
+
+/*
+ * Attention backward: the gradients of O with respect to Q, K and V for an upstream
+ * gradient dO.  The Triton tutorial (sections 2.4 and 4.4) states the method - P is not
+ * kept; the backward pass recomputes it from the forward pass's inputs and statistics
+ * and applies the chain rule - without writing the rule out.  Written out for
+ * O = softmax(scale Q K^T) V (LSE is an auxiliary output and receives no gradient):
+ *
+ *   P     = softmax(scale Q K^T)                 row by row, the three standard steps
+ *   dV    = P^T dO
+ *   dP    = dO V^T
+ *   dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)      the Jacobian of each row's softmax
+ *   dQ    = scale dS K
+ *   dK    = scale dS^T Q
+ *
+ *   dout:  float32 [B, H, N, d] (the gradient of the float32 output O)
+ *   heads: indices b*H + h to compute, ascending (NULL = every head), nheads of them
+ *   dq, dk, dv: doubles [nheads, N, d]
+ * Returns 0, or a negative code for invalid arguments.  Cost B*H*N^2*d: small inputs,
+ * or a few heads.
+ */
+int oracle_attention_bwd(const void *q, const void *k, const void *v, const float *dout,
+                         int dtype, int64_t B, int64_t H, int64_t N, int64_t d, double scale,
+                         const int64_t *heads, int64_t nheads, double *dq, double *dk,
+                         double *dv)
+{
+    int rc = check_common(q, k, v, dtype, B, H, N, d);
+    if (rc)
+        return rc;
+    if (!heads)
+        nheads = B * H;
+    if (!dout || !dq || !dk || !dv || nheads < 0)
+        return -4;
+    for (int64_t x = 0; x < nheads; ++x) {
+        int64_t hd = heads ? heads[x] : x;
+        if (hd < 0 || hd >= B * H || (x > 0 && heads && heads[x] <= heads[x - 1]))
+            return -5;
+    }
+    int fail = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : fail)
+    for (int64_t x = 0; x < nheads; ++x) {
+        const int64_t head = heads ? heads[x] : x;
+        double *Qd = (double *)malloc(sizeof(double) * N * d);
+        double *Kd = (double *)malloc(sizeof(double) * N * d);
+        double *Vd = (double *)malloc(sizeof(double) * N * d);
+        double *dOd = (double *)malloc(sizeof(double) * N * d);
+        double *prow = (double *)malloc(sizeof(double) * N);
+        double *dprow = (double *)malloc(sizeof(double) * N);
+        double *orow = (double *)malloc(sizeof(double) * d);
+        if (!Qd || !Kd || !Vd || !dOd || !prow || !dprow || !orow) {
+            fail = 1;
+        } else {
+            widen_head(q, dtype, head, N, d, Qd);
+            widen_head(k, dtype, head, N, d, Kd);
+            widen_head(v, dtype, head, N, d, Vd);
+            for (int64_t t = 0; t < N * d; ++t)
+                dOd[t] = (double)dout[head * N * d + t];
+            double *dQh = dq + x * N * d, *dKh = dk + x * N * d, *dVh = dv + x * N * d;
+            for (int64_t t = 0; t < N * d; ++t)
+                dQh[t] = dKh[t] = dVh[t] = 0.0;
+            for (int64_t i = 0; i < N; ++i) {
+                const double *qi = Qd + i * d, *gi = dOd + i * d;
+                double lse;
+                row_three_step(qi, Kd, Vd, N, d, scale, NULL, prow, orow, &lse); /* P row i */
+                /* dP_ij = <dO_i, v_j> and the row term sum_k P_ik dP_ik */
+                double Di = 0.0;
+                for (int64_t j = 0; j < N; ++j) {
+                    const double *vj = Vd + j * d;
+                    double acc = 0.0;
+                    for (int64_t t = 0; t < d; ++t)
+                        acc += gi[t] * vj[t];
+                    dprow[j] = acc;
+                    Di += prow[j] * acc;
+                }
+                for (int64_t j = 0; j < N; ++j) {
+                    const double ds = prow[j] * (dprow[j] - Di);
+                    const double *kj = Kd + j * d;
+                    double *dkj = dKh + j * d, *dvj = dVh + j * d;
+                    for (int64_t t = 0; t < d; ++t) {
+                        dQh[i * d + t] += scale * ds * kj[t];
+                        dkj[t] += scale * ds * qi[t];
+                        dvj[t] += prow[j] * gi[t];
+                    }
+                }
+            }
+        }
+        free(Qd);
+        free(Kd);
+        free(Vd);
+        free(dOd);
+        free(prow);
+        free(dprow);
+        free(orow);
+    }
+    return fail ? -6 : 0;
 }
 
 /* number of OpenMP threads a parallel region of this library will use */

@@ -83,6 +83,17 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int, mult: float 
     return out
 
 
+def make_dout(B: int, H: int, N: int, d: int, seed: int, mult: float = 1.0) -> np.ndarray:
+    """Upstream gradient dO of the float32 output O for the backward pass: float32
+    [B, H, N, d] drawn iid N(0, 1) (times ``mult``) from ``Generator(PCG64(seed))``.
+    Callers pass a seed distinct from the one that drew Q, K, V."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    if mult != 1.0:
+        x *= np.float32(mult)
+    return x
+
+
 def to_torch(bits: np.ndarray, dtype: str):
     """Wrap storage bits as a torch CPU tensor of the matching dtype (no copy of values)."""
     import torch

@@ -13,7 +13,11 @@ Sources of truth used here, none of which call into the oracle's code:
     the plain mean;
   * invariants: rows of P sum to one, joint K/V row permutation, key shift;
   * the online-softmax recurrences agree with the full-row max and sum-exp after
-    every block, and reach the three-step O and LSE.
+    every block, and reach the three-step O and LSE;
+  * backward: torch autograd in float64 on the CPU, central finite differences of the
+    forward oracle, closed forms (dO = 0; equal V rows give dQ = dK = 0; one key
+    gives dV = dO) and invariants (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i, key
+    shift leaves every gradient unchanged).
 """
 from __future__ import annotations
 
@@ -233,6 +237,130 @@ def pin_online_equals_three_step():
             assert np.abs(lse - l3).max() <= 1e-12 * np.abs(l3).max()
 
 
+# ---------------------------------------------------------------- backward
+# The backward oracle is tied to torch's autograd (float64, CPU: a library routine that
+# shares nothing with the oracle), to central finite differences of the forward oracle
+# (which the pins above tie down), and to closed forms and invariants of the gradient.
+def _torch_grads(q, k, v, dout, dtype, scale):
+    import torch
+
+    qf, kf, vf = (torch.tensor(_f64(a, dtype), requires_grad=True) for a in (q, k, v))
+    p = torch.softmax(scale * (qf @ kf.transpose(-1, -2)), dim=-1)
+    o = p @ vf
+    o.backward(torch.tensor(dout.astype(np.float64)))
+    return qf.grad.numpy(), kf.grad.numpy(), vf.grad.numpy()
+
+
+def _rel_err(a, b):
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-300))
+
+
+def pin_bwd_torch_autograd():
+    from synth.inputs import make_dout
+
+    for (B, H, N, d, dtype, mult, seed) in [(1, 2, 7, 5, "f32", 1.0, 51), (2, 1, 33, 16, "bf16", 1.0, 52),
+                                            (1, 1, 64, 64, "f16", 2.0, 53), (1, 2, 20, 8, "f32", 4.0, 54)]:
+        x = make_qkv(B, H, N, d, dtype, seed, mult)
+        g = make_dout(B, H, N, d, seed + 1000)
+        scale = 1.0 / math.sqrt(d)
+        ours = oracle.attention_bwd(x["q"], x["k"], x["v"], g, dtype, scale)
+        ref = _torch_grads(x["q"], x["k"], x["v"], g, dtype, scale)
+        for name, a, b in zip(("dq", "dk", "dv"), ours, ref):
+            e = _rel_err(a, b)
+            assert e < 1e-11, f"{name} vs torch autograd ({B},{H},{N},{d},{dtype}): {e:.3e}"
+    # a subset of heads returns exactly those heads
+    x = make_qkv(2, 3, 9, 4, "f32", 55)
+    g = make_dout(2, 3, 9, 4, 1055)
+    full = oracle.attention_bwd(x["q"], x["k"], x["v"], g, "f32", 0.5)
+    part = oracle.attention_bwd(x["q"], x["k"], x["v"], g, "f32", 0.5, heads=[1, 4])
+    for a, b in zip(full, part):
+        assert np.array_equal(a.reshape(6, 9, 4)[[1, 4]], b)
+
+
+def pin_bwd_finite_differences():
+    """Central differences of L = sum(O * dO) through the forward oracle, on float32
+    inputs (the step actually taken is the float32-rounded one)."""
+    from synth.inputs import make_dout
+
+    B, H, N, d = 1, 2, 5, 3
+    x = make_qkv(B, H, N, d, "f32", 61)
+    g = make_dout(B, H, N, d, 1061)
+    scale = 0.7
+    grads = dict(zip("qkv", oracle.attention_bwd(x["q"], x["k"], x["v"], g, "f32", scale)))
+
+    def loss(xx):
+        o, _ = oracle.attention(xx["q"], xx["k"], xx["v"], "f32", scale)
+        return float(np.sum(o * g.astype(np.float64)))
+
+    for name in "qkv":
+        fd = np.empty((B, H, N, d))
+        for idx in np.ndindex(B, H, N, d):
+            x0 = float(x[name][idx])
+            vals = []
+            for sgn in (+1, -1):
+                xx = {n: x[n].copy() for n in "qkv"}
+                xx[name][idx] = np.float32(x0 + sgn * 1e-3)
+                vals.append((loss(xx), float(xx[name][idx])))
+            (lp, xp), (lm, xm) = vals
+            fd[idx] = (lp - lm) / (xp - xm)
+        e = np.abs(fd - grads[name]).max() / np.abs(grads[name]).max()
+        assert e < 1e-5, f"d{name} vs finite differences: {e:.3e}"
+
+
+def pin_bwd_closed_forms():
+    from synth.inputs import make_dout
+
+    B, H, N, d = 1, 2, 24, 8
+    x = make_qkv(B, H, N, d, "f32", 71, mult=2.0)
+    scale = 1.0 / math.sqrt(d)
+    # dO = 0: every gradient is zero
+    z = np.zeros((B, H, N, d), np.float32)
+    for a in oracle.attention_bwd(x["q"], x["k"], x["v"], z, "f32", scale):
+        assert not np.any(a)
+    g = make_dout(B, H, N, d, 1071)
+    # every V row the same: O is that row whatever P is, so dQ = dK = 0, and
+    # sum_j dV_j = sum_i dO_i (the rows of P sum to one)
+    xc = dict(x)
+    xc["v"] = np.ascontiguousarray(np.broadcast_to(x["v"][:, :, :1], x["v"].shape))
+    dq, dk, dv = oracle.attention_bwd(xc["q"], xc["k"], xc["v"], g, "f32", scale)
+    tiny = 1e-12 * np.abs(g).max() * np.abs(_f64(x["k"], "f32")).max()
+    assert np.abs(dq).max() < tiny and np.abs(dk).max() < tiny, (np.abs(dq).max(), np.abs(dk).max())
+    assert np.allclose(dv.sum(axis=2), g.astype(np.float64).sum(axis=2), rtol=0, atol=1e-12)
+    # one key: P = 1, so dV = the sum of dO over the (single) query and dQ = dK = 0
+    x1 = make_qkv(1, 1, 1, 6, "f32", 72)
+    g1 = make_dout(1, 1, 1, 6, 1072)
+    dq, dk, dv = oracle.attention_bwd(x1["q"], x1["k"], x1["v"], g1, "f32", 0.3)
+    assert not np.any(dq) and not np.any(dk)
+    assert np.array_equal(dv, g1.astype(np.float64))
+
+
+def pin_bwd_invariants():
+    from synth.inputs import make_dout
+
+    B, H, N, d = 2, 1, 37, 12
+    x = make_qkv(B, H, N, d, "f32", 81, mult=1.5)
+    g = make_dout(B, H, N, d, 1081)
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = oracle.attention_bwd(x["q"], x["k"], x["v"], g, "f32", scale)
+    mag = np.abs(dk).max()
+    # each row of dS sums to zero, so sum_j dK_j = scale * sum_i (sum_j dS_ij) q_i = 0
+    assert np.abs(dk.sum(axis=2)).max() < 1e-12 * N * mag
+    # the rows of P sum to one: sum_j dV_j = sum_i dO_i
+    assert np.allclose(dv.sum(axis=2), g.astype(np.float64).sum(axis=2), rtol=0, atol=1e-11)
+    # key shift K + 1 u^T moves every score of a row by the same amount: P, dS and all
+    # three gradients are unchanged (dQ because the rows of dS sum to zero).  Keys and
+    # shift lie on a 2^-8 grid, so the shifted keys are exact in float32.
+    grid = lambda a: (np.round(np.asarray(a, np.float64) * 256) / 256).astype(np.float32)
+    k0 = grid(x["k"])
+    u = grid(np.random.Generator(np.random.PCG64(82)).standard_normal(d))
+    k1 = (k0 + u).astype(np.float32)
+    assert np.array_equal(k1.astype(np.float64), k0.astype(np.float64) + u.astype(np.float64))
+    base = oracle.attention_bwd(x["q"], k0, x["v"], g, "f32", scale)
+    moved = oracle.attention_bwd(x["q"], k1, x["v"], g, "f32", scale)
+    for name, a, b in zip(("dq", "dk", "dv"), moved, base):
+        assert _rel_err(a, b) < 1e-10, f"key shift changed {name}: {_rel_err(a, b):.3e}"
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_scipy_softmax_logsumexp,
@@ -245,4 +373,8 @@ ALL_PINS = [
     pin_permutation_invariance,
     pin_key_shift,
     pin_online_equals_three_step,
+    pin_bwd_torch_autograd,
+    pin_bwd_finite_differences,
+    pin_bwd_closed_forms,
+    pin_bwd_invariants,
 ]

@@ -36,6 +36,19 @@ MUTANTS = [
     ("double alpha = exp(m - m_ij);", "double alpha = exp(m_ij - m);", "online rescale sign"),
     ("Oi[t] *= alpha;", "Oi[t] *= 1.0;", "online O rescale dropped"),
     ("l = alpha * l + rowsum;", "l = l + rowsum;", "online l rescale dropped"),
+    # backward (oracle_attention_bwd)
+    ("const double ds = prow[j] * (dprow[j] - Di);", "const double ds = prow[j] * dprow[j];",
+     "softmax Jacobian row term dropped"),
+    ("const double ds = prow[j] * (dprow[j] - Di);", "const double ds = prow[j] * (Di - dprow[j]);",
+     "dS sign flipped"),
+    ("Di += prow[j] * acc;", "Di += acc;", "row term not weighted by P"),
+    ("acc += gi[t] * vj[t];", "acc += gi[t] * vj[d - 1 - t];", "wrong V column in dP"),
+    ("dQh[i * d + t] += scale * ds * kj[t];", "dQh[i * d + t] += scale * ds * qi[t];",
+     "dQ built from Q instead of K"),
+    ("dkj[t] += scale * ds * qi[t];", "dkj[t] += ds * qi[t];", "scale dropped from dK"),
+    ("dvj[t] += prow[j] * gi[t];", "dvj[t] += ds * gi[t];", "dV built from dS instead of P"),
+    ("dOd[t] = (double)dout[head * N * d + t];", "dOd[t] = (double)dout[t];",
+     "dO of head 0 used for every head"),
 ]
 
 
