@@ -23,8 +23,8 @@ STATUS = {
     8: "FA_ERR_HIP",
 }
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_status_string", "fa_version",
-           "fa_last_hip_error")
+EXPORTS = ("fa_fwd", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes",
+           "fa_status_string", "fa_version", "fa_last_hip_error")
 
 _lib = None
 
@@ -52,6 +52,10 @@ def load():
     lib.fa_naive_fwd.restype = I
     lib.fa_naive_workspace_bytes.argtypes = [I, I, I, I]
     lib.fa_naive_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P]
+    lib.fa_bwd.restype = I
+    lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []

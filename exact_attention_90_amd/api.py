@@ -5,6 +5,7 @@ in the library's HIP kernels.  The function names follow the C boundary:
 
     fwd(q, k, v, scale=None)        -> (o, lse)   fused FlashAttention forward
     naive_fwd(q, k, v, scale=None)  -> (o, lse)   materialised S/P contrast path
+    bwd(q, k, v, o, lse, dout)      -> (dq, dk, dv)  backward pass (recomputes P)
 
 q, k, v: contiguous [B, H, N, d] device tensors of one dtype (float32, float16 or
 bfloat16), d in {64, 128, 256}.  o is float32 [B, H, N, d]; lse is float32 [B, H, N]
@@ -101,6 +102,39 @@ def naive_fwd(q, k, v, scale: float | None = None, out=None, lse=None, workspace
                           _CODES[q.dtype], _stream(q, stream))
     _lib.check(rc, "fa_naive_fwd")
     return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype) -> int:
+    code = _CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.load().fa_bwd_workspace_bytes(B, H, N, d, code))
+
+
+def bwd(q, k, v, o, lse, dout, scale: float | None = None, workspace=None, stream=None):
+    """Attention backward: returns (dq, dk, dv), float32 tensors shaped like q.
+
+    o and lse are fwd()'s outputs for the same q, k, v and scale; dout is the float32
+    gradient of o.  workspace: optional uint8 device tensor of at least
+    bwd_workspace_bytes(B, H, N, d, dtype) bytes, 256-byte aligned (allocated when
+    omitted)."""
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for name, t, shape in (("o", o, q.shape), ("dout", dout, q.shape), ("lse", lse, q.shape[:3])):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.shape != shape
+                or not t.is_contiguous() or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous float32 {tuple(shape)} tensor on {q.device}")
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    nbytes = bwd_workspace_bytes(B, H, N, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("backward workspace too small")
+    lib = _lib.load()
+    rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                    workspace.data_ptr(), B, H, N, d, scale, _CODES[q.dtype], _stream(q, stream))
+    _lib.check(rc, "fa_bwd")
+    return dq, dk, dv
 
 
 def version() -> str:

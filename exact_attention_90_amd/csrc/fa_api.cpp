@@ -113,16 +113,84 @@ int fa_naive_fwd(const void *q, const void *k, const void *v, float *o, float *l
                                      p_ws, static_cast<hipStream_t>(stream)));
 }
 
+// Workspace of the backward pass: dO in the input type, then lse2 and D (one float per
+// row each), every part starting on a 256-byte boundary.
+namespace {
+struct BwdLayout {
+  unsigned __int128 do16, lse2, d, total;
+};
+unsigned __int128 round256(unsigned __int128 n) { return (n + 255) / 256 * 256; }
+BwdLayout bwd_layout(int B, int H, int N, int d, int dtype) {
+  const unsigned __int128 rows = (unsigned __int128)(uint64_t)B * (uint64_t)H * (uint64_t)N;
+  BwdLayout L;
+  L.do16 = 0;
+  L.lse2 = round256(rows * (uint64_t)d * (uint64_t)elem_bytes(dtype));
+  L.d = L.lse2 + round256(rows * 4);
+  L.total = L.d + round256(rows * 4);
+  return L;
+}
+bool bwd_supported(int d, int dtype) {
+  return (dtype == FA_F16 || dtype == FA_BF16) && (d == 64 || d == 128);
+}
+}  // namespace
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  if (!bwd_supported(d, dtype) || B < 0 || H < 0 || N < 0) return 0;
+  const unsigned __int128 t = bwd_layout(B, H, N, d, dtype).total;
+  if (t > (unsigned __int128)std::numeric_limits<size_t>::max())
+    return std::numeric_limits<size_t>::max();
+  return (size_t)t;
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const float *o, const float *lse,
+           const float *dout, float *dq, float *dk, float *dv, void *workspace, int B, int H,
+           int N, int d, float scale, int dtype, void *stream) {
+  bool empty = false;
+  int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
+  if (rc != FA_OK) return rc;
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (empty) return FA_OK;
+  if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return FA_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 256)) return FA_ERR_WORKSPACE;
+  rc = device_ready();
+  if (rc != FA_OK) return rc;
+  const BwdLayout L = bwd_layout(B, H, N, d, dtype);
+  char *ws = static_cast<char *>(workspace);
+  fa::BwdProblem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.ws_do16 = ws + (size_t)L.do16;
+  p.ws_lse2 = reinterpret_cast<float *>(ws + (size_t)L.lse2);
+  p.ws_d = reinterpret_cast<float *>(ws + (size_t)L.d);
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.dtype = dtype;
+  return hip_status(fa::launch_bwd(p, static_cast<hipStream_t>(stream)));
+}
+
 const char *fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid or too large B, H or N";
-    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
-    case FA_ERR_DTYPE: return "unknown dtype";
+    case FA_ERR_HEADDIM: return "head dimension not supported (64, 128, 256; backward 64, 128)";
+    case FA_ERR_DTYPE: return "dtype not supported (backward: FA_F16, FA_BF16)";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
-    case FA_ERR_WORKSPACE: return "naive-path workspace NULL or misaligned";
+    case FA_ERR_WORKSPACE: return "workspace NULL or misaligned";
     case FA_ERR_HIP: return "HIP error (no device or launch failure)";
     default: return "unknown status";
   }

@@ -1,0 +1,453 @@
+// Attention backward pass for gfx950: dQ, dK and dV of O = softmax(scale Q K^T) V.
+//
+// Method (pwwt.cn Triton tutorial, sections 2.4 and 4.4): P is never stored; the
+// backward pass recomputes it from the inputs and the forward pass's row statistic
+// (LSE = m + ln l), then applies the chain rule:
+//
+//   P   = exp(scale S - LSE)              S = Q K^T, recomputed tile by tile
+//   dV  = P^T dO
+//   dP  = dO V^T
+//   D_i = <dO_i, O_i>                     (= sum_j P_ij dP_ij, the softmax Jacobian's
+//                                          row term, from the stored output)
+//   dS  = P * (dP - D)
+//   dQ  = scale dS K,   dK = scale dS^T Q
+//
+// Three kernels, every contraction on the matrix cores (v_mfma_f32_32x32x16 in the input
+// type with fp32 accumulation; P and dS are rounded to the input type for theirs):
+//   prep   D_i, LSE_i log2(e), and dO rounded to the input type (one pass over O, dO)
+//   dkdv   one workgroup per 32W keys of a head, each wave owning 32 keys: its K and V
+//          rows stay in registers while Q and dO tiles stream through LDS; dK and dV
+//          accumulate in registers (the lane owns a key, like the query in the forward)
+//   dq     one workgroup per 32W queries: its Q and dO rows stay in registers while K
+//          and V tiles stream through LDS; dQ accumulates in registers
+// No atomics: every output element is written once, so results are deterministic.
+#include "fa_internal.h"
+#include "fa_softmax.hpp"
+
+namespace fa {
+
+// A streamed tile is read two ways: 16-byte row reads (the A operand of S = Q K^T and
+// dP = dO V^T) and transposing reads (the A operand of dV^T = dO^T P and dK^T = Q^T dS,
+// or of dQ^T = K^T dS^T).  One XOR key per row serves both without bank conflicts: over
+// any 16 consecutive rows it is a bijection (the row reads), and its bits that select
+// the 64-byte block differ across 4 consecutive rows (the transposing reads).
+template <int CPR>
+__device__ __forceinline__ int swz_both(int r) {
+  if constexpr (CPR == 8)
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  else
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <bool BF16>
+__device__ __forceinline__ uint32_t pack16(float a, float b) {
+  if constexpr (BF16)
+    return pack_bf16(a, b);
+  else
+    return pack_f16(a, b);
+}
+// the two 16-bit values of a packed word, widened exactly to fp32
+template <bool BF16>
+__device__ __forceinline__ void unpack16(uint32_t w, float &a, float &b) {
+  if constexpr (BF16) {
+    a = __builtin_bit_cast(float, w << 16);
+    b = __builtin_bit_cast(float, w & 0xffff0000u);
+  } else {
+    const f16x2 v = __builtin_bit_cast(f16x2, w);
+    a = (float)v[0];
+    b = (float)v[1];
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// prep: per row, D = <dO, O>, lse2 = LSE log2(e); dO rounded to the input type.  D takes
+// dO as rounded for the dP product, so that sum_j P_ij dP_ij = D_i holds for the values
+// the matrix cores multiply (up to the forward pass's own rounding in O).
+// ------------------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void fa_bwd_prep_kernel(const float *__restrict__ O,
+                                                          const float *__restrict__ dO,
+                                                          const float *__restrict__ LSE,
+                                                          uint16_t *__restrict__ dO16,
+                                                          float *__restrict__ lse2,
+                                                          float *__restrict__ Dv, int64_t rows) {
+  constexpr int TPR = D / 4;  // threads per row, 16 bytes of O and dO each
+  const int64_t total = rows * TPR;
+  for (int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x; gid - threadIdx.x < total;
+       gid += int64_t(gridDim.x) * 256) {
+    // every thread of a row runs the same iterations (rows never straddle a block)
+    const int64_t row = gid / TPR;
+    const int c = int(gid % TPR);
+    float part = 0.f;
+    if (row < rows) {
+      const f32x4 o = *reinterpret_cast<const f32x4 *>(O + row * D + 4 * c);
+      const f32x4 g = *reinterpret_cast<const f32x4 *>(dO + row * D + 4 * c);
+      const u32x2 gw = {pack16<BF16>(g[0], g[1]), pack16<BF16>(g[2], g[3])};
+      *reinterpret_cast<u32x2 *>(dO16 + row * D + 4 * c) = gw;
+      float r0, r1, r2, r3;
+      unpack16<BF16>(gw[0], r0, r1);
+      unpack16<BF16>(gw[1], r2, r3);
+      part = o[0] * r0 + o[1] * r1 + o[2] * r2 + o[3] * r3;
+    }
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) part += __shfl_xor(part, off);
+    if (row < rows && c == 0) {
+      Dv[row] = part;
+      lse2[row] = LSE[row] * kLog2e;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// shared configuration of the two main kernels
+// ------------------------------------------------------------------------------------
+template <int D, int WAVES>
+struct CfgB {
+  static constexpr int NT = 64 * WAVES;        // threads per workgroup
+  static constexpr int BR = 32 * WAVES;        // resident rows (keys or queries) per workgroup
+  static constexpr int BT = 64;                // rows per streamed tile
+  static constexpr int ROWB = 2 * D;           // bytes per 16-bit row
+  static constexpr int CPR = ROWB / 16;        // 16-byte chunks per row
+  static constexpr int TILEB = BT * ROWB;      // bytes of one streamed tile
+  static constexpr int CPT = TILEB / 16 / NT;  // chunks per thread per tile
+  static constexpr int KC = D / 16;            // k-steps over d
+  static constexpr int OB = D / 32;            // 32-column output blocks
+  static constexpr int RSTEP = NT / CPR;       // rows between a thread's chunks
+  static constexpr int STATB = 1024;           // one statistics stage (64 lanes x 16 B)
+  static constexpr int LDS = 4 * TILEB + 4 * STATB;
+  static_assert(CPT >= 1 && TILEB % (16 * NT) == 0, "a tile is whole chunks per thread");
+  static_assert(RSTEP % 16 == 0, "a thread's rows share one swizzle key");
+  static_assert(32 * D * 4 <= LDS / WAVES, "a wave's output rows fit its LDS share");
+};
+
+// Lane offsets into a streamed tile (bytes, without the stage offset):
+//   row reads: row 32t + l32, logical chunk 2kc + h  ->  rb + 32t ROWB + ((32kc) ^ rx)
+//   transposing reads for k-step u (rows 16u + 8x + ...), output block e:
+//                                                     ->  tb[x] + 16u ROWB + ((64e) ^ tx)
+template <int CPR, int ROWB>
+struct TileLanes {
+  int rb, rx, tb0, tb1, tx;
+  __device__ __forceinline__ TileLanes(int lane) {
+    const int h = lane >> 5, l32 = lane & 31;
+    const int f = swz_both<CPR>(l32);  // rows 32t + l32 share the key of l32
+    rb = l32 * ROWB + 16 * (h ^ (f & 1));
+    rx = 32 * (f >> 1);
+    // transposing read: lane j of 16-lane group G reads row 8x + 4(G/2) + j/4 (plus 16u)
+    // at columns 32e + 16(G%2) + 4(j%4): chunk 4e + c0, byte (column % 8) * 2
+    const int grp = lane >> 4, j16 = lane & 15;
+    const int r0 = 4 * (grp >> 1) + (j16 >> 2);
+    const int col = 16 * (grp & 1) + 4 * (j16 & 3);
+    const int c0 = col >> 3, cb = (col & 7) * 2;
+    const int f0 = swz_both<CPR>(r0), f1 = swz_both<CPR>(r0 + 8);
+    // chunk (4e + c0) ^ f = 4 (e ^ (f >> 2)) + (c0 ^ (f & 3)); f >> 2 is the same for
+    // rows r0 and r0 + 8
+    tb0 = r0 * ROWB + 16 * (c0 ^ (f0 & 3)) + cb;
+    tb1 = (r0 + 8) * ROWB + 16 * (c0 ^ (f1 & 3)) + cb;
+    tx = 64 * (f0 >> 2);
+  }
+};
+
+// ------------------------------------------------------------------------------------
+// dkdv: dK and dV for the 32W keys of one workgroup
+// ------------------------------------------------------------------------------------
+template <int D>
+constexpr int dkdv_wpe() { return D == 128 ? 1 : 2; }
+
+template <int D, bool BF16, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO16,
+    const float *__restrict__ lse2, const float *__restrict__ Dv, float *__restrict__ dK,
+    float *__restrict__ dV, int N, int nkb, int G, float c, float scale) {
+  using C = CfgB<D, WAVES>;
+  constexpr int KC = C::KC, OB = C::OB, CPT = C::CPT;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char *const Qs = smem;                    // Q tiles, two stages
+  char *const Gs = smem + 2 * C::TILEB;     // dO tiles, two stages
+  char *const Ls = smem + 4 * C::TILEB;     // lse2 of the tile's queries, two stages
+  char *const Ds = Ls + 2 * C::STATB;       // D of the tile's queries, two stages
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int L = xcd_remap(blockIdx.x, G);
+  const int bh = L / nkb, k0 = (L % nkb) * C::BR;
+  const int64_t hoff = int64_t(bh) * N * D;
+  const uint32_t head_bytes = uint32_t(N) * C::ROWB;
+  const auto qrs = make_rsrc(Q + hoff, head_bytes);
+  const auto grs = make_rsrc(dO16 + hoff, head_bytes);
+  const auto krs = make_rsrc(K + hoff, head_bytes);
+  const auto vrs = make_rsrc(V + hoff, head_bytes);
+  const auto lrs = make_rsrc(lse2 + int64_t(bh) * N, uint32_t(N) * 4);
+  const auto drs = make_rsrc(Dv + int64_t(bh) * N, uint32_t(N) * 4);
+
+  // the wave's 32 keys: K and V rows as B operands (lane: key l32, columns 8h.. of each
+  // 16-column k-step); keys past N read zeros
+  const int key = k0 + 32 * w + l32;
+  u32x4 kf[KC], vf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    kf[kc] = buf_load16(krs, key * C::ROWB + (2 * kc + h) * 16, 0);
+    vf[kc] = buf_load16(vrs, key * C::ROWB + (2 * kc + h) * 16, 0);
+  }
+
+  const TileLanes<C::CPR, C::ROWB> tl(lane);
+  // loads of a tile into LDS: chunk i of thread tid is LDS chunk i NT + tid, i.e. row
+  // i RSTEP + tid / CPR at physical chunk tid % CPR, which holds logical chunk
+  // (tid % CPR) ^ key(row); every row of a thread has the same key
+  const int srow = tid / C::CPR, sch = tid % C::CPR;
+  const int st_off = srow * C::ROWB + (sch ^ swz_both<C::CPR>(srow)) * 16;
+  constexpr int ST_STEP = C::NT * 16;
+  const int dma_wave = wu * 1024;
+  auto load_tile = [&](int stage, int qt) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      buf_load16_lds(qrs, Qs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off,
+                     qt * C::TILEB + i * ST_STEP);
+      buf_load16_lds(grs, Gs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off,
+                     qt * C::TILEB + i * ST_STEP);
+    }
+    // the tile's 64 values of lse2 and D (lanes 16..63 bring bytes no one reads)
+    if (wu == 0) buf_load16_lds(lrs, Ls + stage * C::STATB, lane * 16, qt * 256);
+    if (wu == WAVES - 1) buf_load16_lds(drs, Ds + stage * C::STATB, lane * 16, qt * 256);
+  };
+
+  f32x16 dk[OB], dv[OB];
+#pragma unroll
+  for (int e = 0; e < OB; ++e) dk[e] = dv[e] = f32x16{};
+
+  const int nqt = (N + C::BT - 1) / C::BT;
+  load_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  lds_barrier();
+  for (int qt = 0; qt < nqt; ++qt) {
+    const int st = qt & 1;
+    // the other stage held tile qt - 1, released by the barrier that ended it
+    if (qt + 1 < nqt) load_tile(st ^ 1, qt + 1);
+    const int qb = st * C::TILEB;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {  // 32-query blocks of the tile
+      // S = Q K^T and dP = dO V^T for queries 32t + (8(r/4) + 4h + r%4), key l32
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int off = qb + tl.rb + 32 * t * C::ROWB + ((32 * kc) ^ tl.rx);
+        s = mma16<BF16>(lds_read16(Qs, off), kf[kc], s);
+        dp = mma16<BF16>(lds_read16(Gs, off), vf[kc], dp);
+      }
+      // P = 2^(c s - lse2_q), dS = P (dP - D_q); the statistics of queries
+      // 32t + 8g + 4h + 0..3 are one 16-byte broadcast read each
+      float p[16], ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qo = (32 * t + 8 * g + 4 * h) * 4;
+        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(Ls + st * C::STATB + qo);
+        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(Ds + st * C::STATB + qo);
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int r = 4 * g + s4;
+          p[r] = ex2(fmaf(s[r], c, -l4[s4]));
+          ds[r] = p[r] * (dp[r] - d4[s4]);
+        }
+      }
+      // operands of k-steps 2t, 2t + 1: registers 8x .. 8x + 7 hold queries
+      // 16(2t + x) + 8y + 4h + s4 in slot 4y + s4
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int rb = 8 * x;
+        const u32x4 pf = {pack16<BF16>(p[rb + 0], p[rb + 1]), pack16<BF16>(p[rb + 2], p[rb + 3]),
+                          pack16<BF16>(p[rb + 4], p[rb + 5]), pack16<BF16>(p[rb + 6], p[rb + 7])};
+        const u32x4 sf = {pack16<BF16>(ds[rb + 0], ds[rb + 1]), pack16<BF16>(ds[rb + 2], ds[rb + 3]),
+                          pack16<BF16>(ds[rb + 4], ds[rb + 5]), pack16<BF16>(ds[rb + 6], ds[rb + 7])};
+        const int u = 2 * t + x;
+#pragma unroll
+        for (int e = 0; e < OB; ++e) {
+          const int o0 = qb + tl.tb0 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
+          const int o1 = qb + tl.tb1 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
+          const u32x2 g0 = lds_read_tr(Gs, o0), g1 = lds_read_tr(Gs, o1);
+          const u32x2 q0 = lds_read_tr(Qs, o0), q1 = lds_read_tr(Qs, o1);
+          dv[e] = mma16<BF16>(u32x4{g0[0], g0[1], g1[0], g1[1]}, pf, dv[e]);
+          dk[e] = mma16<BF16>(u32x4{q0[0], q0[1], q1[0], q1[1]}, sf, dk[e]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));  // tile qt + 1 has landed
+    lds_barrier();
+  }
+
+  // dK = scale dK^T (the lane's key column), dV; each through the wave's LDS share
+  constexpr int WAVE_LDS = (C::LDS / WAVES) & ~15;
+  const int row0 = k0 + 32 * w;
+  char *region = smem + w * WAVE_LDS;
+  // store_rows_lds divides by the pair sum of its normaliser: 1/scale for dK, 1 for dV
+  store_rows_lds<D, 1>(dk, 0.f, 1.f, 0.5f / scale, region, dK + hoff + int64_t(row0) * D,
+                       nullptr, lane, N - row0);
+  store_rows_lds<D, 1>(dv, 0.f, 1.f, 0.5f, region, dV + hoff + int64_t(row0) * D, nullptr,
+                       lane, N - row0);
+}
+
+// ------------------------------------------------------------------------------------
+// dq: dQ for the 32W queries of one workgroup
+// ------------------------------------------------------------------------------------
+template <int D, bool BF16, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 2) void fa_bwd_dq_kernel(
+    const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
+    const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO16,
+    const float *__restrict__ lse2, const float *__restrict__ Dv, float *__restrict__ dQ, int N,
+    int nqb, int G, float c, float scale) {
+  using C = CfgB<D, WAVES>;
+  constexpr int KC = C::KC, OB = C::OB, CPT = C::CPT;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char *const Ks = smem;                 // K tiles, two stages
+  char *const Vs = smem + 2 * C::TILEB;  // V tiles, two stages
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int L = xcd_remap(blockIdx.x, G);
+  const int bh = L / nqb, q0 = (L % nqb) * C::BR;
+  const int64_t hoff = int64_t(bh) * N * D;
+  const uint32_t head_bytes = uint32_t(N) * C::ROWB;
+  const auto qrs = make_rsrc(Q + hoff, head_bytes);
+  const auto grs = make_rsrc(dO16 + hoff, head_bytes);
+  const auto krs = make_rsrc(K + hoff, head_bytes);
+  const auto vrs = make_rsrc(V + hoff, head_bytes);
+
+  // the wave's 32 queries: Q and dO rows as B operands, and the row statistics
+  const int row = q0 + 32 * w + l32;
+  u32x4 qf[KC], gf[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    qf[kc] = buf_load16(qrs, row * C::ROWB + (2 * kc + h) * 16, 0);
+    gf[kc] = buf_load16(grs, row * C::ROWB + (2 * kc + h) * 16, 0);
+  }
+  const float my_lse2 = row < N ? lse2[int64_t(bh) * N + row] : 0.f;
+  const float my_d = row < N ? Dv[int64_t(bh) * N + row] : 0.f;
+
+  const TileLanes<C::CPR, C::ROWB> tl(lane);
+  const int srow = tid / C::CPR, sch = tid % C::CPR;
+  const int st_off = srow * C::ROWB + (sch ^ swz_both<C::CPR>(srow)) * 16;
+  constexpr int ST_STEP = C::NT * 16;
+  const int dma_wave = wu * 1024;
+  auto load_tile = [&](int stage, int kt) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      buf_load16_lds(krs, Ks + stage * C::TILEB + dma_wave + i * ST_STEP, st_off,
+                     kt * C::TILEB + i * ST_STEP);
+      buf_load16_lds(vrs, Vs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off,
+                     kt * C::TILEB + i * ST_STEP);
+    }
+  };
+
+  f32x16 dq[OB];
+#pragma unroll
+  for (int e = 0; e < OB; ++e) dq[e] = f32x16{};
+
+  const int nkt = (N + C::BT - 1) / C::BT;
+  load_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+  lds_barrier();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nkt) load_tile(st ^ 1, kt + 1);
+    const int kb = st * C::TILEB;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {  // 32-key blocks of the tile
+      // S^T = K Q^T and dP^T = V dO^T: keys 32t + (8(r/4) + 4h + r%4), query l32.  Keys
+      // past N read zero K and V rows, so their dS meets a zero K row below and adds
+      // nothing to dQ.
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int off = kb + tl.rb + 32 * t * C::ROWB + ((32 * kc) ^ tl.rx);
+        s = mma16<BF16>(lds_read16(Ks, off), qf[kc], s);
+        dp = mma16<BF16>(lds_read16(Vs, off), gf[kc], dp);
+      }
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = ex2(fmaf(s[r], c, -my_lse2)) * (dp[r] - my_d);
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int rb = 8 * x;
+        const u32x4 sf = {pack16<BF16>(ds[rb + 0], ds[rb + 1]), pack16<BF16>(ds[rb + 2], ds[rb + 3]),
+                          pack16<BF16>(ds[rb + 4], ds[rb + 5]), pack16<BF16>(ds[rb + 6], ds[rb + 7])};
+        const int u = 2 * t + x;
+#pragma unroll
+        for (int e = 0; e < OB; ++e) {
+          // dQ^T += K^T dS^T: K^T rows are the tile's key rows read transposed
+          const int o0 = kb + tl.tb0 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
+          const int o1 = kb + tl.tb1 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
+          const u32x2 a0 = lds_read_tr(Ks, o0), a1 = lds_read_tr(Ks, o1);
+          dq[e] = mma16<BF16>(u32x4{a0[0], a0[1], a1[0], a1[1]}, sf, dq[e]);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    lds_barrier();
+  }
+
+  constexpr int WAVE_LDS = (C::LDS / WAVES) & ~15;
+  const int row0 = q0 + 32 * w;
+  store_rows_lds<D, 1>(dq, 0.f, 1.f, 0.5f / scale, smem + w * WAVE_LDS,
+                       dQ + hoff + int64_t(row0) * D, nullptr, lane, N - row0);
+}
+
+// ------------------------------------------------------------------------------------
+template <typename KernelT>
+static hipError_t allow_lds_bwd(KernelT kernel, int bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <int D, bool BF16>
+static hipError_t run_bwd(const BwdProblem &p, hipStream_t stream) {
+  constexpr int WAVES = 4;
+  using C = CfgB<D, WAVES>;
+  const int64_t rows = int64_t(p.B) * p.H * p.N;
+  uint16_t *dO16 = static_cast<uint16_t *>(p.ws_do16);
+  // prep
+  {
+    const int64_t blocks = (rows * (D / 4) + 255) / 256;
+    const int grid = int(blocks < kMaxGrid ? blocks : kMaxGrid);
+    hipLaunchKernelGGL((fa_bwd_prep_kernel<D, BF16>), dim3(grid), dim3(256), 0, stream, p.o,
+                       p.dout, p.lse, dO16, p.ws_lse2, p.ws_d, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const float c = p.scale * kLog2e;
+  const int nb = (p.N + C::BR - 1) / C::BR;
+  const int G = nb * p.B * p.H;
+  {
+    auto kern = fa_bwd_dkdv_kernel<D, BF16, WAVES>;
+    static const hipError_t attr = allow_lds_bwd(kern, C::LDS);
+    (void)attr;
+    hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
+                       static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
+                       static_cast<const uint16_t *>(p.v), dO16, p.ws_lse2, p.ws_d, p.dk, p.dv,
+                       p.N, nb, G, c, p.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    auto kern = fa_bwd_dq_kernel<D, BF16, WAVES>;
+    static const hipError_t attr = allow_lds_bwd(kern, C::LDS);
+    (void)attr;
+    hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
+                       static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
+                       static_cast<const uint16_t *>(p.v), dO16, p.ws_lse2, p.ws_d, p.dq, p.N,
+                       nb, G, c, p.scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream) {
+  if (p.dtype == kBF16) return p.d == 128 ? run_bwd<128, true>(p, stream) : run_bwd<64, true>(p, stream);
+  return p.d == 128 ? run_bwd<128, false>(p, stream) : run_bwd<64, false>(p, stream);
+}
+
+}  // namespace fa

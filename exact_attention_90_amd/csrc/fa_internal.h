@@ -27,7 +27,21 @@ constexpr int64_t kMaxGrid = int64_t(1) << 24;
 // offsets and may read one tile (<= 64 KiB) past its end (those reads return zeros).
 constexpr int64_t kMaxHeadBytes = (int64_t(1) << 31) - (int64_t(1) << 17);
 
+// Backward pass: inputs, outputs and the caller's workspace split into its three parts
+// (dO rounded to the input type, lse2 = LSE log2(e), D = rowsum(dO O)).
+struct BwdProblem {
+  const void *q, *k, *v;
+  const float *o, *lse, *dout;
+  float *dq, *dk, *dv;
+  void *ws_do16;
+  float *ws_lse2, *ws_d;
+  int B, H, N, d;
+  float scale;
+  int dtype;
+};
+
 hipError_t launch_fused(const Problem &p, hipStream_t stream);
+hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream);
 hipError_t launch_naive(const Problem &p, void *s_ws, void *p_ws, hipStream_t stream);
 
 }  // namespace fa

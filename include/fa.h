@@ -53,11 +53,11 @@ enum fa_status {
     FA_ERR_NULL = 1,      /* a required pointer is NULL (and the problem is not empty) */
     FA_ERR_SHAPE = 2,     /* B, H or N negative, or too large: B*H*ceil(N/128) > 2^24
                              workgroups, or one head's N*d*elem > 2^31 - 2^17 bytes */
-    FA_ERR_HEADDIM = 3,   /* d is not 64, 128 or 256 */
-    FA_ERR_DTYPE = 4,     /* dtype is not one of fa_dtype */
+    FA_ERR_HEADDIM = 3,   /* d is not 64, 128 or 256 (fa_bwd: 64 or 128) */
+    FA_ERR_DTYPE = 4,     /* dtype is not one of fa_dtype (fa_bwd: FA_F16 or FA_BF16) */
     FA_ERR_SCALE = 5,     /* scale is not a finite number > 0 */
     FA_ERR_ALIGN = 6,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
-    FA_ERR_WORKSPACE = 7, /* naive path: a workspace pointer is NULL or misaligned */
+    FA_ERR_WORKSPACE = 7, /* a workspace pointer is NULL or misaligned */
     FA_ERR_HIP = 8        /* no usable HIP device, or a launch failed; see fa_last_hip_error */
 };
 
@@ -116,6 +116,47 @@ int fa_naive_fwd(const void *q, const void *k, const void *v, float *o, float *l
  * SIZE_MAX if the product does not fit in size_t.
  */
 size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype);
+
+/*
+ * fa_bwd - attention backward: the gradients of O with respect to Q, K and V.
+ *
+ * The method is the recomputation of the pwwt.cn Triton tutorial (sections 2.4 and
+ * 4.4): P is not stored; it is rebuilt tile by tile from q, k and the forward pass's
+ * lse, and the chain rule gives, for the upstream gradient dO of O,
+ *     dV = P^T dO,  dP = dO V^T,  D_i = <dO_i, O_i>,  dS = P * (dP - D),
+ *     dQ = scale dS K,  dK = scale dS^T Q.
+ * LSE is an auxiliary output and receives no gradient.
+ *
+ *   q, k, v    as for fa_fwd; dtype FA_F16 or FA_BF16 only, d = 64 or 128 only.
+ *   o, lse     fa_fwd's outputs for the same q, k, v and scale (device, float32).
+ *   dout       device pointer, [B, H, N, d] float32, 16-byte aligned: dO.
+ *   dq, dk, dv device pointers, [B, H, N, d] float32, 16-byte aligned, not overlapping
+ *              any input: receive the gradients.
+ *   workspace  device pointer of at least fa_bwd_workspace_bytes(B, H, N, d, dtype)
+ *              bytes, 256-byte aligned, owned by the caller, not overlapping any tensor.
+ *              It receives dO rounded to the input type and two floats per row.
+ *   B, H, N, scale, stream as for fa_fwd.
+ *
+ * Precision: every product runs on the matrix cores in the input type with float32
+ * accumulation; dO, P and dS are rounded to the input type (round to nearest even)
+ * for the products that take them; D and the softmax statistics are float32.
+ * Three kernels run in order on `stream`; results are bitwise identical from run to
+ * run (no atomics).
+ *
+ * Returns FA_OK, or (before any launch) the error codes of fa_fwd, FA_ERR_DTYPE for
+ * FA_F32, FA_ERR_HEADDIM for d = 256, FA_ERR_NULL for a NULL dout/dq/dk/dv,
+ * FA_ERR_ALIGN, or FA_ERR_WORKSPACE for a NULL or misaligned workspace.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const float *o, const float *lse,
+           const float *dout, float *dq, float *dk, float *dv, void *workspace, int B, int H,
+           int N, int d, float scale, int dtype, void *stream);
+
+/*
+ * Bytes of the backward workspace: B*H*N*d*sizeof(dtype) + 8*B*H*N, each of its three
+ * parts rounded up to a multiple of 256.  Returns 0 for a combination fa_bwd does not
+ * support or a negative size, and SIZE_MAX if the total does not fit in size_t.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);

@@ -98,6 +98,31 @@ def test_empty_problem_is_a_no_op(lib, kwargs):
     assert call(lib, **kwargs) == 0
 
 
+def bwd_call(lib, dtype=1, d=64, ws=0x8000, dout=0x9000, dq=0xa000, N=128):
+    return lib.fa_bwd(A, B_, C_, O_, L_, dout, dq, 0xb000, 0xc000, ws, 1, 1, N, d, 0.125, dtype,
+                      None)
+
+
+def test_bwd_rejects_unsupported_and_bad_arguments(lib):
+    assert bwd_call(lib, dtype=0) == 4          # fp32 inputs: no backward kernel
+    assert bwd_call(lib, d=256) == 3            # d = 256: no backward kernel
+    assert bwd_call(lib, d=96) == 3
+    assert bwd_call(lib, ws=0) == 7             # NULL workspace
+    assert bwd_call(lib, ws=0x8010) == 7        # workspace not 256-byte aligned
+    assert bwd_call(lib, dout=0) == 1
+    assert bwd_call(lib, dq=0xa004) == 6
+    assert bwd_call(lib, N=0, ws=0, dout=0, dq=0) == 0  # empty problem
+
+
+def test_bwd_workspace_bytes(lib):
+    # dO in the input type plus two floats per row, each part rounded up to 256 bytes
+    assert lib.fa_bwd_workspace_bytes(8, 32, 4096, 128, 2) == 8 * 32 * 4096 * (128 * 2 + 8)
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 64, 1) == 512 + 256 + 256  # 384 B of dO -> 512
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 64, 0) == 0      # unsupported
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 256, 1) == 0
+    assert lib.fa_bwd_workspace_bytes(-1, 1, 3, 64, 1) == 0
+
+
 def test_naive_rejects_bad_workspace(lib):
     args = (A, B_, C_, O_, L_)
     assert lib.fa_naive_fwd(*args, None, 0x6000, 1, 1, 64, 64, 0.125, 1, None) == 7
