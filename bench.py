@@ -2,6 +2,7 @@
 """Throughput of the fused attention forward (fa_fwd) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3] [--path fused|naive]
+    python bench.py --pass bwd [--workload c3]     the backward pass (fa_bwd) instead
 
 One step is one fa_fwd call over the whole workload (all B*H heads, all N query
 rows).  Inputs are seeded synthetic tensors already resident in device memory when
@@ -38,12 +39,17 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # MI355X dense matr
 KERNEL_SOURCES = ("exact_attention_90_amd/csrc/fa_fused.hip",
                   "exact_attention_90_amd/csrc/fa_softmax.hpp",
                   "exact_attention_90_amd/csrc/fa_device.hpp")
+# the backward kernels have their own hash (bench --pass bwd), so that a change to them
+# does not invalidate the forward pass's committed counters
+BWD_KERNEL_SOURCES = ("exact_attention_90_amd/csrc/fa_bwd.hip",
+                      "exact_attention_90_amd/csrc/fa_softmax.hpp",
+                      "exact_attention_90_amd/csrc/fa_device.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.md")
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -54,7 +60,7 @@ def committed_traffic(workload: str, path: str):
     summary is missing or was taken on different kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    src = kernel_source_hash()
+    src = kernel_source_hash(BWD_KERNEL_SOURCES if path == "bwd" else KERNEL_SOURCES)
     for line in open(TRAFFIC_FILE):
         m = re.match(r"\s*traffic-json:\s*(\{.*\})\s*$", line)
         if not m:
@@ -194,6 +200,10 @@ def main() -> int:
     ap.add_argument("--shape", default=None, metavar="B,H,N,d,dtype",
                     help="measure an ad-hoc shape instead of a named workload (N(0,1) inputs)")
     ap.add_argument("--path", default="fused", choices=["fused", "naive"])
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="fwd: the forward pass (the headline); bwd: the backward pass "
+                         "(fa_bwd, 16-bit inputs, d 64 or 128), counted as five N x N x d "
+                         "products (10 B H N^2 d flops)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -235,6 +245,8 @@ def main() -> int:
     q, k, v = (to_torch(x[n], w.dtype).to(dev) for n in ("q", "k", "v"))
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    if args.which == "bwd":
+        return bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev)
     ws = None
     if args.path == "naive":
         nb = fa.naive_workspace_bytes(w.B, w.H, w.N, q.dtype)
@@ -314,6 +326,99 @@ def main() -> int:
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
         base, parity = cpu_baseline(x, w, o, lse, args.cpu_seconds)
+        line["cpu_baseline"] = base
+        line["parity_sample"] = parity
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline_bwd(x, dout, w, grads_gpu, target_heads: int):
+    """The backward oracle, unchanged, on whole heads (the gradients of a key depend on
+    every query): the first `target_heads` heads, one per OpenMP thread.  Returns the
+    baseline record and the parity of the GPU's gradients on those heads."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.num_threads()
+    nh = max(1, min(w.B * w.H, target_heads))
+    heads = list(range(nh))
+    t0 = time.perf_counter()
+    ref = oracle.attention_bwd(x["q"], x["k"], x["v"], dout, w.dtype,
+                               float(np.float32(w.scale)), heads=heads)
+    dt = time.perf_counter() - t0
+    flops = 10.0 * nh * w.N * w.N * w.d
+    parity = {}
+    for name, g, r in zip(("dq", "dk", "dv"), grads_gpu, ref):
+        a = g.reshape(w.B * w.H, w.N, w.d)[:nh].cpu().numpy().astype(np.float64)
+        e = a - r
+        parity[name] = {"rms_rel": float(np.linalg.norm(e) / np.linalg.norm(r)),
+                        "max_rel": float(np.abs(e).max() / np.abs(r).max())}
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nh} of {w.B * w.H} heads of {w.short()}, every query and key of "
+                      f"each (10 N^2 d flops per head); fp64 C oracle, {dt:.1f} s"}
+    return base, parity
+
+
+def bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev):
+    """Time fa_bwd (prep + dK/dV + dQ kernels) on the workload; one JSON line."""
+    import torch
+
+    import exact_attention_90_amd as fa
+    from synth.inputs import make_dout
+
+    if w.dtype == "f32" or w.d not in (64, 128) or args.path != "fused":
+        print("bench.py: the backward pass takes fp16/bf16 inputs with d 64 or 128",
+              file=sys.stderr)
+        return 2
+    g_np = make_dout(w.B, w.H, w.N, w.d, w.seed + 5000)
+    g = torch.from_numpy(g_np).to(dev)
+    fa.fwd(q, k, v, scale32, out=o, lse=lse)
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8,
+                     device=dev)
+    grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+
+    def step():
+        fa.bwd(q, k, v, o, lse, g, scale32, workspace=ws, grads=grads)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize(dev)
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    flops = 10.0 * w.B * w.H * w.N * w.N * w.d
+    value = flops / (ms_step * 1e-3) / 1e12
+    avg = sum(per) / len(per)
+    peak = PEAK_TFLOPS[w.dtype]
+    rec = committed_traffic(w.name, "bwd")
+    line = {
+        "metric": f"bwd attention TFLOP/s (5 products, 10 B H N^2 d), {w.short()}",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: attention backward (dQ, dK, dV from O, LSE, dO), "
+                               f"{w.short()}, scale 1/sqrt({w.d})",
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "path": "fused",
+                   "parallelism": "single GPU"},
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(flops / (avg * 1e-3) / 1e12, 3),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(flops / (avg * 1e-3) / 1e12 / peak, 4),
+                     "traffic": rec.get("bytes_per_launch") if rec else None,
+                     "kernel": "fa_bwd (prep + dkdv + dq kernels)",
+                     "avg_launch_ms": round(avg, 5), "min_launch_ms": round(min(per), 5),
+                     "kernel_src": kernel_source_hash(BWD_KERNEL_SOURCES)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        base, parity = cpu_baseline_bwd(x, g_np, w, grads, target_heads=16)
         line["cpu_baseline"] = base
         line["parity_sample"] = parity
     print(json.dumps(line), flush=True)

@@ -109,13 +109,14 @@ def bwd_workspace_bytes(B: int, H: int, N: int, d: int, dtype) -> int:
     return int(_lib.load().fa_bwd_workspace_bytes(B, H, N, d, code))
 
 
-def bwd(q, k, v, o, lse, dout, scale: float | None = None, workspace=None, stream=None):
+def bwd(q, k, v, o, lse, dout, scale: float | None = None, workspace=None, grads=None,
+        stream=None):
     """Attention backward: returns (dq, dk, dv), float32 tensors shaped like q.
 
     o and lse are fwd()'s outputs for the same q, k, v and scale; dout is the float32
     gradient of o.  workspace: optional uint8 device tensor of at least
     bwd_workspace_bytes(B, H, N, d, dtype) bytes, 256-byte aligned (allocated when
-    omitted)."""
+    omitted).  grads: optional (dq, dk, dv) float32 tensors to write into."""
     _check_inputs(q, k, v)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -123,7 +124,12 @@ def bwd(q, k, v, o, lse, dout, scale: float | None = None, workspace=None, strea
         if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.shape != shape
                 or not t.is_contiguous() or t.device != q.device):
             raise ValueError(f"{name} must be a contiguous float32 {tuple(shape)} tensor on {q.device}")
-    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    if grads is None:
+        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    dq, dk, dv = grads
+    for t in grads:
+        if t.dtype != torch.float32 or t.shape != q.shape or not t.is_contiguous():
+            raise ValueError("grads must be contiguous float32 tensors shaped like q")
     nbytes = bwd_workspace_bytes(B, H, N, d, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)

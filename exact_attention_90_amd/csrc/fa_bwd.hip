@@ -285,9 +285,9 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
   const int row0 = k0 + 32 * w;
   char *region = smem + w * WAVE_LDS;
   // store_rows_lds divides by the pair sum of its normaliser: 1/scale for dK, 1 for dV
-  store_rows_lds<D, 1>(dk, 0.f, 1.f, 0.5f / scale, region, dK + hoff + int64_t(row0) * D,
+  store_rows_lds<D, 1, false>(dk, 0.f, 1.f, 0.5f / scale, region, dK + hoff + int64_t(row0) * D,
                        nullptr, lane, N - row0);
-  store_rows_lds<D, 1>(dv, 0.f, 1.f, 0.5f, region, dV + hoff + int64_t(row0) * D, nullptr,
+  store_rows_lds<D, 1, false>(dv, 0.f, 1.f, 0.5f, region, dV + hoff + int64_t(row0) * D, nullptr,
                        lane, N - row0);
 }
 
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_bwd_dq_kernel(
 
   constexpr int WAVE_LDS = (C::LDS / WAVES) & ~15;
   const int row0 = q0 + 32 * w;
-  store_rows_lds<D, 1>(dq, 0.f, 1.f, 0.5f / scale, smem + w * WAVE_LDS,
+  store_rows_lds<D, 1, false>(dq, 0.f, 1.f, 0.5f / scale, smem + w * WAVE_LDS,
                        dQ + hoff + int64_t(row0) * D, nullptr, lane, N - row0);
 }
 

@@ -96,10 +96,11 @@ __device__ __forceinline__ void store_rows(f32x16 (&o)[OB], float mc, float l, f
 // wave touches it), then reads it back row-contiguous so that every store instruction
 // writes whole rows of O (whole 128-byte lines).  NHALF > 1 stages the columns in
 // parts when the region holds only part of a row.  nvalid = rows of this wave that
-// exist (rows >= nvalid are not written).  lse0 == nullptr writes no LSE (the backward
-// pass stores its gradients through the same path, with lnorm choosing the factor).  Within one wave LDS accesses complete in
+// exist (rows >= nvalid are not written).  Within one wave LDS accesses complete in
 // order, so no barrier is needed between the write, the read and the next part.
-template <int D, int NHALF>
+// WITH_LSE = false writes no LSE: the backward pass stores its gradients this way, with
+// lnorm choosing the factor.
+template <int D, int NHALF, bool WITH_LSE = true>
 __device__ __forceinline__ void store_rows_lds(f32x16 (&o)[D / 32], float mc, float l,
                                                float lnorm, char *wave_lds, float *orow0,
                                                float *lse0, int lane, int nvalid) {
@@ -111,7 +112,7 @@ __device__ __forceinline__ void store_rows_lds(f32x16 (&o)[D / 32], float mc, fl
   const int h = lane >> 5, l32 = lane & 31;
   const float lt = pair_sum(l);  // both halves of the row hold partial sums
   const float inv = 1.0f / pair_sum(lnorm);
-  if (lse0 != nullptr && h == 0 && l32 < nvalid) lse0[l32] = (mc + lg2(lt)) * kLn2;
+  if (WITH_LSE && h == 0 && l32 < nvalid) lse0[l32] = (mc + lg2(lt)) * kLn2;
   // chunk c of row r sits at chunk c ^ (r % 16) of the row: the 8 rows a write phase
   // covers land on distinct banks, and a read of whole rows is a permutation
 #pragma unroll
