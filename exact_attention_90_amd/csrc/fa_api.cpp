@@ -130,7 +130,7 @@ BwdLayout bwd_layout(int B, int H, int N, int d, int dtype) {
   return L;
 }
 bool bwd_supported(int d, int dtype) {
-  return (dtype == FA_F16 || dtype == FA_BF16) && (d == 64 || d == 128);
+  return (dtype == FA_F16 || dtype == FA_BF16) && (d == 64 || d == 128 || d == 256);
 }
 }  // namespace
 
@@ -149,7 +149,6 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
   int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
   if (rc != FA_OK) return rc;
   if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
   if (empty) return FA_OK;
   if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
@@ -186,7 +185,7 @@ const char *fa_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid or too large B, H or N";
-    case FA_ERR_HEADDIM: return "head dimension not supported (64, 128, 256; backward 64, 128)";
+    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
     case FA_ERR_DTYPE: return "dtype not supported (backward: FA_F16, FA_BF16)";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";

@@ -21,6 +21,8 @@
 //   dq     one workgroup per 32W queries: its Q and dO rows stay in registers while K
 //          and V tiles stream through LDS; dQ accumulates in registers
 // No atomics: every output element is written once, so results are deterministic.
+#include <type_traits>
+
 #include "fa_internal.h"
 #include "fa_softmax.hpp"
 
@@ -118,10 +120,13 @@ struct CfgB {
   static constexpr int KC = D / 16;            // k-steps over d
   static constexpr int OB = D / 32;            // 32-column output blocks
   static constexpr int RSTEP = NT / CPR;       // rows between a thread's chunks
+  // with 512-byte rows (d = 256) a thread's rows are 8 apart and their swizzle keys
+  // alternate between two values
+  static constexpr bool KFLIP = RSTEP % 16 != 0;
   static constexpr int STATB = 1024;           // one statistics stage (64 lanes x 16 B)
   static constexpr int LDS = 4 * TILEB + 4 * STATB;
   static_assert(CPT >= 1 && TILEB % (16 * NT) == 0, "a tile is whole chunks per thread");
-  static_assert(RSTEP % 16 == 0, "a thread's rows share one swizzle key");
+  static_assert(RSTEP % 8 == 0, "a thread's rows alternate between at most two keys");
   static_assert(32 * D * 4 <= LDS / WAVES, "a wave's output rows fit its LDS share");
 };
 
@@ -153,12 +158,19 @@ struct TileLanes {
 };
 
 // ------------------------------------------------------------------------------------
-// dkdv: dK and dV for the 32W keys of one workgroup
+// dkdv: dK and dV for the 32W keys of one workgroup.  WHAT selects the outputs
+// (kDK | kDV): at d = 256 the rows of K, V, dK and dV of 32 keys exceed a SIMD's
+// registers, so dV and dK are computed by two launches (each recomputes S).
 // ------------------------------------------------------------------------------------
+constexpr int kDK = 1, kDV = 2;
+// minimum waves per SIMD the registers must allow (K, V, dK and dV rows of 32 keys take
+// 6 d / 4 registers per lane)
 template <int D>
-constexpr int dkdv_wpe() { return D == 128 ? 1 : 2; }
+constexpr int dkdv_wpe() { return D >= 128 ? 1 : 2; }
+template <int D>
+constexpr int dq_wpe() { return D >= 256 ? 1 : 2; }
 
-template <int D, bool BF16, int WAVES>
+template <int D, bool BF16, int WAVES, int WHAT>
 __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO16,
@@ -188,12 +200,13 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
 
   // the wave's 32 keys: K and V rows as B operands (lane: key l32, columns 8h.. of each
   // 16-column k-step); keys past N read zeros
+  constexpr bool WANT_DK = (WHAT & kDK) != 0, WANT_DV = (WHAT & kDV) != 0;
   const int key = k0 + 32 * w + l32;
-  u32x4 kf[KC], vf[KC];
+  u32x4 kf[KC], vf[WANT_DK ? KC : 1];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
     kf[kc] = buf_load16(krs, key * C::ROWB + (2 * kc + h) * 16, 0);
-    vf[kc] = buf_load16(vrs, key * C::ROWB + (2 * kc + h) * 16, 0);
+    if constexpr (WANT_DK) vf[kc] = buf_load16(vrs, key * C::ROWB + (2 * kc + h) * 16, 0);
   }
 
   const TileLanes<C::CPR, C::ROWB> tl(lane);
@@ -201,25 +214,32 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
   // i RSTEP + tid / CPR at physical chunk tid % CPR, which holds logical chunk
   // (tid % CPR) ^ key(row); every row of a thread has the same key
   const int srow = tid / C::CPR, sch = tid % C::CPR;
-  const int st_off = srow * C::ROWB + (sch ^ swz_both<C::CPR>(srow)) * 16;
+  const int st_off0 = srow * C::ROWB + (sch ^ swz_both<C::CPR>(srow)) * 16;
+  const int st_off1 =
+      C::KFLIP ? srow * C::ROWB + (sch ^ swz_both<C::CPR>(srow + C::RSTEP)) * 16 : st_off0;
+  auto st_off = [&](int i) { return (C::KFLIP && (i & 1)) ? st_off1 : st_off0; };
   constexpr int ST_STEP = C::NT * 16;
   const int dma_wave = wu * 1024;
   auto load_tile = [&](int stage, int qt) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      buf_load16_lds(qrs, Qs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off,
+      buf_load16_lds(qrs, Qs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
                      qt * C::TILEB + i * ST_STEP);
-      buf_load16_lds(grs, Gs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off,
+      buf_load16_lds(grs, Gs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
                      qt * C::TILEB + i * ST_STEP);
     }
     // the tile's 64 values of lse2 and D (lanes 16..63 bring bytes no one reads)
     if (wu == 0) buf_load16_lds(lrs, Ls + stage * C::STATB, lane * 16, qt * 256);
-    if (wu == WAVES - 1) buf_load16_lds(drs, Ds + stage * C::STATB, lane * 16, qt * 256);
+    if (WANT_DK && wu == WAVES - 1)
+      buf_load16_lds(drs, Ds + stage * C::STATB, lane * 16, qt * 256);
   };
 
-  f32x16 dk[OB], dv[OB];
+  f32x16 dk[WANT_DK ? OB : 1], dv[WANT_DV ? OB : 1];
 #pragma unroll
-  for (int e = 0; e < OB; ++e) dk[e] = dv[e] = f32x16{};
+  for (int e = 0; e < OB; ++e) {
+    if constexpr (WANT_DK) dk[e] = f32x16{};
+    if constexpr (WANT_DV) dv[e] = f32x16{};
+  }
 
   const int nqt = (N + C::BT - 1) / C::BT;
   load_tile(0, 0);
@@ -238,7 +258,7 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
       for (int kc = 0; kc < KC; ++kc) {
         const int off = qb + tl.rb + 32 * t * C::ROWB + ((32 * kc) ^ tl.rx);
         s = mma16<BF16>(lds_read16(Qs, off), kf[kc], s);
-        dp = mma16<BF16>(lds_read16(Gs, off), vf[kc], dp);
+        if constexpr (WANT_DK) dp = mma16<BF16>(lds_read16(Gs, off), vf[kc], dp);
       }
       // P = 2^(c s - lse2_q), dS = P (dP - D_q); the statistics of queries
       // 32t + 8g + 4h + 0..3 are one 16-byte broadcast read each
@@ -247,12 +267,13 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
       for (int g = 0; g < 4; ++g) {
         const int qo = (32 * t + 8 * g + 4 * h) * 4;
         const f32x4 l4 = *reinterpret_cast<const f32x4 *>(Ls + st * C::STATB + qo);
-        const f32x4 d4 = *reinterpret_cast<const f32x4 *>(Ds + st * C::STATB + qo);
+        f32x4 d4 = {};
+        if constexpr (WANT_DK) d4 = *reinterpret_cast<const f32x4 *>(Ds + st * C::STATB + qo);
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const int r = 4 * g + s4;
           p[r] = ex2(fmaf(s[r], c, -l4[s4]));
-          ds[r] = p[r] * (dp[r] - d4[s4]);
+          ds[r] = WANT_DK ? p[r] * (dp[r] - d4[s4]) : 0.f;
         }
       }
       // operands of k-steps 2t, 2t + 1: registers 8x .. 8x + 7 hold queries
@@ -269,10 +290,14 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
         for (int e = 0; e < OB; ++e) {
           const int o0 = qb + tl.tb0 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
           const int o1 = qb + tl.tb1 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
-          const u32x2 g0 = lds_read_tr(Gs, o0), g1 = lds_read_tr(Gs, o1);
-          const u32x2 q0 = lds_read_tr(Qs, o0), q1 = lds_read_tr(Qs, o1);
-          dv[e] = mma16<BF16>(u32x4{g0[0], g0[1], g1[0], g1[1]}, pf, dv[e]);
-          dk[e] = mma16<BF16>(u32x4{q0[0], q0[1], q1[0], q1[1]}, sf, dk[e]);
+          if constexpr (WANT_DV) {
+            const u32x2 g0 = lds_read_tr(Gs, o0), g1 = lds_read_tr(Gs, o1);
+            dv[e] = mma16<BF16>(u32x4{g0[0], g0[1], g1[0], g1[1]}, pf, dv[e]);
+          }
+          if constexpr (WANT_DK) {
+            const u32x2 q0 = lds_read_tr(Qs, o0), q1 = lds_read_tr(Qs, o1);
+            dk[e] = mma16<BF16>(u32x4{q0[0], q0[1], q1[0], q1[1]}, sf, dk[e]);
+          }
         }
       }
     }
@@ -285,17 +310,19 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
   const int row0 = k0 + 32 * w;
   char *region = smem + w * WAVE_LDS;
   // store_rows_lds divides by the pair sum of its normaliser: 1/scale for dK, 1 for dV
-  store_rows_lds<D, 1, false>(dk, 0.f, 1.f, 0.5f / scale, region, dK + hoff + int64_t(row0) * D,
-                       nullptr, lane, N - row0);
-  store_rows_lds<D, 1, false>(dv, 0.f, 1.f, 0.5f, region, dV + hoff + int64_t(row0) * D, nullptr,
-                       lane, N - row0);
+  if constexpr (WANT_DK)
+    store_rows_lds<D, 1, false>(dk, 0.f, 1.f, 0.5f / scale, region,
+                                dK + hoff + int64_t(row0) * D, nullptr, lane, N - row0);
+  if constexpr (WANT_DV)
+    store_rows_lds<D, 1, false>(dv, 0.f, 1.f, 0.5f, region, dV + hoff + int64_t(row0) * D,
+                                nullptr, lane, N - row0);
 }
 
 // ------------------------------------------------------------------------------------
 // dq: dQ for the 32W queries of one workgroup
 // ------------------------------------------------------------------------------------
 template <int D, bool BF16, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, 2) void fa_bwd_dq_kernel(
+__global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO16,
     const float *__restrict__ lse2, const float *__restrict__ Dv, float *__restrict__ dQ, int N,
@@ -331,15 +358,18 @@ __global__ __launch_bounds__(64 * WAVES, 2) void fa_bwd_dq_kernel(
 
   const TileLanes<C::CPR, C::ROWB> tl(lane);
   const int srow = tid / C::CPR, sch = tid % C::CPR;
-  const int st_off = srow * C::ROWB + (sch ^ swz_both<C::CPR>(srow)) * 16;
+  const int st_off0 = srow * C::ROWB + (sch ^ swz_both<C::CPR>(srow)) * 16;
+  const int st_off1 =
+      C::KFLIP ? srow * C::ROWB + (sch ^ swz_both<C::CPR>(srow + C::RSTEP)) * 16 : st_off0;
+  auto st_off = [&](int i) { return (C::KFLIP && (i & 1)) ? st_off1 : st_off0; };
   constexpr int ST_STEP = C::NT * 16;
   const int dma_wave = wu * 1024;
   auto load_tile = [&](int stage, int kt) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      buf_load16_lds(krs, Ks + stage * C::TILEB + dma_wave + i * ST_STEP, st_off,
+      buf_load16_lds(krs, Ks + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
                      kt * C::TILEB + i * ST_STEP);
-      buf_load16_lds(vrs, Vs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off,
+      buf_load16_lds(vrs, Vs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
                      kt * C::TILEB + i * ST_STEP);
     }
   };
@@ -422,15 +452,25 @@ static hipError_t run_bwd(const BwdProblem &p, hipStream_t stream) {
   const float c = p.scale * kLog2e;
   const int nb = (p.N + C::BR - 1) / C::BR;
   const int G = nb * p.B * p.H;
-  {
-    auto kern = fa_bwd_dkdv_kernel<D, BF16, WAVES>;
+  // dK and dV: one launch, or (d = 256) one for dV and one for dK
+  auto dkdv = [&](auto what) -> hipError_t {
+    auto kern = fa_bwd_dkdv_kernel<D, BF16, WAVES, decltype(what)::value>;
     static const hipError_t attr = allow_lds_bwd(kern, C::LDS);
     (void)attr;
     hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
                        static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                        static_cast<const uint16_t *>(p.v), dO16, p.ws_lse2, p.ws_d, p.dk, p.dv,
                        p.N, nb, G, c, p.scale);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+  };
+  {
+    hipError_t e;
+    if constexpr (D == 256) {
+      e = dkdv(std::integral_constant<int, kDV>{});
+      if (e == hipSuccess) e = dkdv(std::integral_constant<int, kDK>{});
+    } else {
+      e = dkdv(std::integral_constant<int, kDK | kDV>{});
+    }
     if (e != hipSuccess) return e;
   }
   {
@@ -446,8 +486,13 @@ static hipError_t run_bwd(const BwdProblem &p, hipStream_t stream) {
 }
 
 hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream) {
-  if (p.dtype == kBF16) return p.d == 128 ? run_bwd<128, true>(p, stream) : run_bwd<64, true>(p, stream);
-  return p.d == 128 ? run_bwd<128, false>(p, stream) : run_bwd<64, false>(p, stream);
+  if (p.dtype == kBF16)
+    return p.d == 256   ? run_bwd<256, true>(p, stream)
+           : p.d == 128 ? run_bwd<128, true>(p, stream)
+                        : run_bwd<64, true>(p, stream);
+  return p.d == 256   ? run_bwd<256, false>(p, stream)
+         : p.d == 128 ? run_bwd<128, false>(p, stream)
+                      : run_bwd<64, false>(p, stream);
 }
 
 }  // namespace fa

@@ -53,7 +53,7 @@ enum fa_status {
     FA_ERR_NULL = 1,      /* a required pointer is NULL (and the problem is not empty) */
     FA_ERR_SHAPE = 2,     /* B, H or N negative, or too large: B*H*ceil(N/128) > 2^24
                              workgroups, or one head's N*d*elem > 2^31 - 2^17 bytes */
-    FA_ERR_HEADDIM = 3,   /* d is not 64, 128 or 256 (fa_bwd: 64 or 128) */
+    FA_ERR_HEADDIM = 3,   /* d is not 64, 128 or 256 */
     FA_ERR_DTYPE = 4,     /* dtype is not one of fa_dtype (fa_bwd: FA_F16 or FA_BF16) */
     FA_ERR_SCALE = 5,     /* scale is not a finite number > 0 */
     FA_ERR_ALIGN = 6,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
@@ -127,7 +127,7 @@ size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype);
  *     dQ = scale dS K,  dK = scale dS^T Q.
  * LSE is an auxiliary output and receives no gradient.
  *
- *   q, k, v    as for fa_fwd; dtype FA_F16 or FA_BF16 only, d = 64 or 128 only.
+ *   q, k, v    as for fa_fwd; dtype FA_F16 or FA_BF16 only (d = 64, 128 or 256).
  *   o, lse     fa_fwd's outputs for the same q, k, v and scale (device, float32).
  *   dout       device pointer, [B, H, N, d] float32, 16-byte aligned: dO.
  *   dq, dk, dv device pointers, [B, H, N, d] float32, 16-byte aligned, not overlapping
@@ -140,11 +140,11 @@ size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype);
  * Precision: every product runs on the matrix cores in the input type with float32
  * accumulation; dO, P and dS are rounded to the input type (round to nearest even)
  * for the products that take them; D and the softmax statistics are float32.
- * Three kernels run in order on `stream`; results are bitwise identical from run to
- * run (no atomics).
+ * Three kernels run in order on `stream` (four at d = 256, where dV and dK take one
+ * launch each); results are bitwise identical from run to run (no atomics).
  *
  * Returns FA_OK, or (before any launch) the error codes of fa_fwd, FA_ERR_DTYPE for
- * FA_F32, FA_ERR_HEADDIM for d = 256, FA_ERR_NULL for a NULL dout/dq/dk/dv,
+ * FA_F32, FA_ERR_NULL for a NULL dout/dq/dk/dv,
  * FA_ERR_ALIGN, or FA_ERR_WORKSPACE for a NULL or misaligned workspace.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const float *o, const float *lse,

@@ -127,6 +127,19 @@ def test_bwd_bitwise_deterministic():
         assert np.array_equal(u, v)
 
 
+# d = 256: dV and dK come from two launches of the key-owned kernel
+@pytest.mark.parametrize("B,H,N,dtype", [(1, 2, 200, "bf16"), (2, 1, 333, "f16"),
+                                         (1, 1, 1000, "bf16"), (1, 2, 1, "f16"),
+                                         (1, 2, 129, "bf16")])
+def test_bwd_d256(B, H, N, dtype):
+    gpu, ref = full_case(B, H, N, 256, dtype, seed=N + 256)
+    if N == 1:
+        tiny = 1e-4 * np.abs(ref[2]).max()
+        assert np.abs(gpu[0]).max() <= tiny and np.abs(gpu[1]).max() <= tiny
+        return
+    assert_grads(gpu, ref, dtype, f"{B}x{H}x{N}x256 {dtype}")
+
+
 def test_bwd_larger_sampled_heads():
     # a larger problem: every gradient of two heads (first and last) against the oracle
     B, H, N, d, dtype = 2, 8, 2048, 128, "bf16"
