@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fused.hip", "fa_naive.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fused.hip", "fa_naive.hip", "fa_bwd.hip", "fa_bwd32.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of every device code object.

@@ -123,13 +123,14 @@ unsigned __int128 round256(unsigned __int128 n) { return (n + 255) / 256 * 256; 
 BwdLayout bwd_layout(int B, int H, int N, int d, int dtype) {
   const unsigned __int128 rows = (unsigned __int128)(uint64_t)B * (uint64_t)H * (uint64_t)N;
   BwdLayout L;
-  L.do16 = 0;
-  L.lse2 = round256(rows * (uint64_t)d * (uint64_t)elem_bytes(dtype));
+  L.do16 = 0;  // fp32 inputs use dO as given: no rounded copy
+  L.lse2 = dtype == FA_F32 ? 0 : round256(rows * (uint64_t)d * 2);
   L.d = L.lse2 + round256(rows * 4);
   L.total = L.d + round256(rows * 4);
   return L;
 }
 bool bwd_supported(int d, int dtype) {
+  if (dtype == FA_F32) return d == 64 || d == 128;
   return (dtype == FA_F16 || dtype == FA_BF16) && (d == 64 || d == 128 || d == 256);
 }
 }  // namespace
@@ -148,7 +149,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
   bool empty = false;
   int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
   if (rc != FA_OK) return rc;
-  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (!bwd_supported(d, dtype)) return FA_ERR_HEADDIM;  // fp32 inputs at d = 256
   if (empty) return FA_OK;
   if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
   if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
@@ -185,8 +186,8 @@ const char *fa_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid or too large B, H or N";
-    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256";
-    case FA_ERR_DTYPE: return "dtype not supported (backward: FA_F16, FA_BF16)";
+    case FA_ERR_HEADDIM: return "head dimension must be 64, 128 or 256 (fp32 backward: 64, 128)";
+    case FA_ERR_DTYPE: return "unknown dtype";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_WORKSPACE: return "workspace NULL or misaligned";

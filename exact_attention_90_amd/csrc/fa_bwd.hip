@@ -486,6 +486,7 @@ static hipError_t run_bwd(const BwdProblem &p, hipStream_t stream) {
 }
 
 hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream) {
+  if (p.dtype == kF32) return launch_bwd32(p, stream);
   if (p.dtype == kBF16)
     return p.d == 256   ? run_bwd<256, true>(p, stream)
            : p.d == 128 ? run_bwd<128, true>(p, stream)

@@ -41,7 +41,8 @@ struct BwdProblem {
 };
 
 hipError_t launch_fused(const Problem &p, hipStream_t stream);
-hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream);
+hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream);    // every dtype
+hipError_t launch_bwd32(const BwdProblem &p, hipStream_t stream);  // fp32 inputs
 hipError_t launch_naive(const Problem &p, void *s_ws, void *p_ws, hipStream_t stream);
 
 }  // namespace fa

@@ -53,8 +53,8 @@ enum fa_status {
     FA_ERR_NULL = 1,      /* a required pointer is NULL (and the problem is not empty) */
     FA_ERR_SHAPE = 2,     /* B, H or N negative, or too large: B*H*ceil(N/128) > 2^24
                              workgroups, or one head's N*d*elem > 2^31 - 2^17 bytes */
-    FA_ERR_HEADDIM = 3,   /* d is not 64, 128 or 256 */
-    FA_ERR_DTYPE = 4,     /* dtype is not one of fa_dtype (fa_bwd: FA_F16 or FA_BF16) */
+    FA_ERR_HEADDIM = 3,   /* d is not 64, 128 or 256 (fa_bwd with FA_F32: 64 or 128) */
+    FA_ERR_DTYPE = 4,     /* dtype is not one of fa_dtype */
     FA_ERR_SCALE = 5,     /* scale is not a finite number > 0 */
     FA_ERR_ALIGN = 6,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
     FA_ERR_WORKSPACE = 7, /* a workspace pointer is NULL or misaligned */
@@ -127,7 +127,7 @@ size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype);
  *     dQ = scale dS K,  dK = scale dS^T Q.
  * LSE is an auxiliary output and receives no gradient.
  *
- *   q, k, v    as for fa_fwd; dtype FA_F16 or FA_BF16 only (d = 64, 128 or 256).
+ *   q, k, v    as for fa_fwd (FA_F32 inputs: d = 64 or 128).
  *   o, lse     fa_fwd's outputs for the same q, k, v and scale (device, float32).
  *   dout       device pointer, [B, H, N, d] float32, 16-byte aligned: dO.
  *   dq, dk, dv device pointers, [B, H, N, d] float32, 16-byte aligned, not overlapping
@@ -138,13 +138,14 @@ size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype);
  *   B, H, N, scale, stream as for fa_fwd.
  *
  * Precision: every product runs on the matrix cores in the input type with float32
- * accumulation; dO, P and dS are rounded to the input type (round to nearest even)
- * for the products that take them; D and the softmax statistics are float32.
+ * accumulation; for FA_F16 and FA_BF16 inputs dO, P and dS are rounded to the input
+ * type (round to nearest even) for the products that take them, for FA_F32 inputs
+ * nothing is rounded below float32; D and the softmax statistics are float32.
  * Three kernels run in order on `stream` (four at d = 256, where dV and dK take one
  * launch each); results are bitwise identical from run to run (no atomics).
  *
- * Returns FA_OK, or (before any launch) the error codes of fa_fwd, FA_ERR_DTYPE for
- * FA_F32, FA_ERR_NULL for a NULL dout/dq/dk/dv,
+ * Returns FA_OK, or (before any launch) the error codes of fa_fwd, FA_ERR_HEADDIM for
+ * FA_F32 inputs with d = 256, FA_ERR_NULL for a NULL dout/dq/dk/dv,
  * FA_ERR_ALIGN, or FA_ERR_WORKSPACE for a NULL or misaligned workspace.
  */
 int fa_bwd(const void *q, const void *k, const void *v, const float *o, const float *lse,
@@ -152,8 +153,8 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
            int N, int d, float scale, int dtype, void *stream);
 
 /*
- * Bytes of the backward workspace: B*H*N*d*sizeof(dtype) + 8*B*H*N, each of its three
- * parts rounded up to a multiple of 256.  Returns 0 for a combination fa_bwd does not
+ * Bytes of the backward workspace: B*H*N*d*2 (dO rounded to a 16-bit input type; none
+ * for FA_F32) + 8*B*H*N, each of its parts rounded up to a multiple of 256.  Returns 0 for a combination fa_bwd does not
  * support or a negative size, and SIZE_MAX if the total does not fit in size_t.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);

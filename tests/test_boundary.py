@@ -104,7 +104,8 @@ def bwd_call(lib, dtype=1, d=64, ws=0x8000, dout=0x9000, dq=0xa000, N=128):
 
 
 def test_bwd_rejects_unsupported_and_bad_arguments(lib):
-    assert bwd_call(lib, dtype=0) == 4          # fp32 inputs: no backward kernel
+    assert bwd_call(lib, dtype=0, d=256) == 3   # fp32 inputs at d = 256: no backward kernel
+    assert bwd_call(lib, dtype=3) == 4
     assert bwd_call(lib, d=96) == 3
     assert bwd_call(lib, d=512) == 3
     assert bwd_call(lib, ws=0) == 7             # NULL workspace
@@ -118,7 +119,8 @@ def test_bwd_workspace_bytes(lib):
     # dO in the input type plus two floats per row, each part rounded up to 256 bytes
     assert lib.fa_bwd_workspace_bytes(8, 32, 4096, 128, 2) == 8 * 32 * 4096 * (128 * 2 + 8)
     assert lib.fa_bwd_workspace_bytes(1, 1, 3, 64, 1) == 512 + 256 + 256  # 384 B of dO -> 512
-    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 64, 0) == 0      # unsupported
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 64, 0) == 256 + 256  # fp32: no dO copy
+    assert lib.fa_bwd_workspace_bytes(1, 1, 3, 256, 0) == 0     # unsupported
     assert lib.fa_bwd_workspace_bytes(1, 1, 3, 256, 1) == 1536 + 256 + 256
     assert lib.fa_bwd_workspace_bytes(1, 1, 3, 96, 1) == 0
     assert lib.fa_bwd_workspace_bytes(-1, 1, 3, 64, 1) == 0

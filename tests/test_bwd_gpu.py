@@ -8,7 +8,9 @@ with u the unit roundoff of the input type (bf16 2^-8, fp16 2^-11).  Every produ
 runs on the matrix cores with two or three of its factors rounded to the input type
 (dO, P, dS; round to nearest even, RMS relative error about 0.58 u each), so the
 expected RMS relative error is about 1-1.5 u; the max over ~10^5 elements of such
-errors stays below ~8 u.  The oracle's result is exact to double rounding.
+errors stays below ~8 u.  For fp32 inputs nothing is rounded below fp32: u = 2^-16
+covers fp32 rounding (2^-24) grown by sums of up to 4096 terms (x 2^6) and the
+hardware exp2 (within 2 ulp, x 4).  The oracle's result is exact to double rounding.
 """
 import math
 
@@ -21,7 +23,7 @@ from tests.gpu_util import say, to_device
 
 pytestmark = pytest.mark.gpu
 
-UNIT = {"bf16": 2.0**-8, "f16": 2.0**-11}
+UNIT = {"bf16": 2.0**-8, "f16": 2.0**-11, "f32": 2.0**-16}
 
 
 def run_bwd(x, dout, dtype, scale):
@@ -138,6 +140,14 @@ def test_bwd_d256(B, H, N, dtype):
         assert np.abs(gpu[0]).max() <= tiny and np.abs(gpu[1]).max() <= tiny
         return
     assert_grads(gpu, ref, dtype, f"{B}x{H}x{N}x256 {dtype}")
+
+
+# fp32 inputs: fp32 matrix cores, nothing rounded below fp32
+@pytest.mark.parametrize("B,H,N,d", [(1, 2, 128, 64), (1, 2, 200, 128), (2, 1, 333, 64),
+                                     (1, 1, 65, 128), (1, 2, 700, 128)])
+def test_bwd_f32(B, H, N, d):
+    gpu, ref = full_case(B, H, N, d, "f32", seed=N + d + 32)
+    assert_grads(gpu, ref, "f32", f"{B}x{H}x{N}x{d} f32")
 
 
 def test_bwd_larger_sampled_heads():
