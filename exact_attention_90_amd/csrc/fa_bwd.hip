@@ -250,53 +250,181 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
     // the other stage held tile qt - 1, released by the barrier that ended it
     if (qt + 1 < nqt) load_tile(st ^ 1, qt + 1);
     const int qb = st * C::TILEB;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {  // 32-query blocks of the tile
-      // S = Q K^T and dP = dO V^T for queries 32t + (8(r/4) + 4h + r%4), key l32
-      f32x16 s = {}, dp = {};
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int off = qb + tl.rb + 32 * t * C::ROWB + ((32 * kc) ^ tl.rx);
-        s = mma16<BF16>(lds_read16(Qs, off), kf[kc], s);
-        if constexpr (WANT_DK) dp = mma16<BF16>(lds_read16(Gs, off), vf[kc], dp);
-      }
-      // P = 2^(c s - lse2_q), dS = P (dP - D_q); the statistics of queries
-      // 32t + 8g + 4h + 0..3 are one 16-byte broadcast read each
-      float p[16], ds[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int qo = (32 * t + 8 * g + 4 * h) * 4;
-        const f32x4 l4 = *reinterpret_cast<const f32x4 *>(Ls + st * C::STATB + qo);
-        f32x4 d4 = {};
-        if constexpr (WANT_DK) d4 = *reinterpret_cast<const f32x4 *>(Ds + st * C::STATB + qo);
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int r = 4 * g + s4;
-          p[r] = ex2(fmaf(s[r], c, -l4[s4]));
-          ds[r] = WANT_DK ? p[r] * (dp[r] - d4[s4]) : 0.f;
-        }
-      }
-      // operands of k-steps 2t, 2t + 1: registers 8x .. 8x + 7 hold queries
-      // 16(2t + x) + 8y + 4h + s4 in slot 4y + s4
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int rb = 8 * x;
-        const u32x4 pf = {pack16<BF16>(p[rb + 0], p[rb + 1]), pack16<BF16>(p[rb + 2], p[rb + 3]),
-                          pack16<BF16>(p[rb + 4], p[rb + 5]), pack16<BF16>(p[rb + 6], p[rb + 7])};
-        const u32x4 sf = {pack16<BF16>(ds[rb + 0], ds[rb + 1]), pack16<BF16>(ds[rb + 2], ds[rb + 3]),
-                          pack16<BF16>(ds[rb + 4], ds[rb + 5]), pack16<BF16>(ds[rb + 6], ds[rb + 7])};
-        const int u = 2 * t + x;
-#pragma unroll
-        for (int e = 0; e < OB; ++e) {
+    if constexpr (D >= 128) {
+      // The tile's two 32-query blocks t = 0, 1 go through three parts:
+      //   A(t)  S = Q K^T and dP = dO V^T for queries 32t + (8(r/4) + 4h + r%4), key l32
+      //         (matrix cores; the tiles read as rows)
+      //   V(t)  P = 2^(c s - lse2_q), dS = P (dP - D_q), both packed into the operand
+      //         layout of B (VALU)
+      //   B(t)  dV^T += dO^T P and dK^T += Q^T dS (matrix cores; the tiles read transposed)
+      // in four phases, A0 | A1 + V0 | B0 + V1 | B1, so that the vector work of one block
+      // rides between the matrix-core steps of the other.  Operand reads run PA (A) and
+      // PB (B) steps ahead, in rings indexed by the step's position in the tile (block t,
+      // step kc is position t KC + kc), so that the next block's first reads never take a
+      // slot this block still needs; fences keep every step in place.
+      {
+        constexpr int PA = 3, PB = 2, NB = 2 * OB;
+        static_assert(PA <= KC && PB <= NB, "prefetch depth within one part");
+        f32x16 s[2], dp[2];
+        float p[2][16], ds[2][16];
+        u32x4 pf[2][2], sf[2][2];
+        f32x4 lq[2][4], dq4[2][4];
+        u32x4 qa[PA], ga[PA], bg[PB], bq[PB];
+        // A operands: rows 32t + l32 of the Q and dO tiles at logical chunk 2kc + h
+        auto a_load = [&](int t, int kc) {
+          const int off = qb + tl.rb + 32 * t * C::ROWB + ((32 * kc) ^ tl.rx);
+          const int slot = (t * KC + kc) % PA;
+          qa[slot] = lds_read16(Qs, off);
+          if constexpr (WANT_DK) ga[slot] = lds_read16(Gs, off);
+        };
+        auto a_step = [&](int t, int kc) {
+          const int slot = (t * KC + kc) % PA;
+          s[t] = mma16<BF16>(qa[slot], kf[kc], kc == 0 ? f32x16{} : s[t]);
+          if constexpr (WANT_DK) dp[t] = mma16<BF16>(ga[slot], vf[kc], kc == 0 ? f32x16{} : dp[t]);
+        };
+        // statistics of the 16 queries block t's registers hold: 32t + 8g + 4h + 0..3
+        auto stat_load = [&](int t) {
+  #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int qo = st * C::STATB + (32 * t + 8 * g + 4 * h) * 4;
+            lq[t][g] = *reinterpret_cast<const f32x4 *>(Ls + qo);
+            if constexpr (WANT_DK) dq4[t][g] = *reinterpret_cast<const f32x4 *>(Ds + qo);
+          }
+        };
+        // V(t) for registers lo .. hi-1; operand block x (registers 8x .. 8x + 7: queries
+        // 16(2t + x) + 8y + 4h + s4 in slot 4y + s4) is packed once its 8 values exist
+        auto v_range = [&](int t, int lo, int hi) {
+  #pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (r >= lo && r < hi) {
+              p[t][r] = ex2(fmaf(s[t][r], c, -lq[t][r >> 2][r & 3]));
+              ds[t][r] = WANT_DK ? p[t][r] * (dp[t][r] - dq4[t][r >> 2][r & 3]) : 0.f;
+            }
+  #pragma unroll
+          for (int x = 0; x < 2; ++x)
+            if (hi >= 8 * x + 8 && lo < 8 * x + 8) {
+              const float *a = p[t] + 8 * x, *b = ds[t] + 8 * x;
+              pf[t][x] = u32x4{pack16<BF16>(a[0], a[1]), pack16<BF16>(a[2], a[3]),
+                               pack16<BF16>(a[4], a[5]), pack16<BF16>(a[6], a[7])};
+              if constexpr (WANT_DK)
+                sf[t][x] = u32x4{pack16<BF16>(b[0], b[1]), pack16<BF16>(b[2], b[3]),
+                                 pack16<BF16>(b[4], b[5]), pack16<BF16>(b[6], b[7])};
+            }
+        };
+        // B step i of block t: k-step u = 2t + i / OB (16 queries), output block e = i % OB
+        auto b_load = [&](int t, int i) {
+          const int u = 2 * t + i / OB, e = i % OB;
           const int o0 = qb + tl.tb0 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
           const int o1 = qb + tl.tb1 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
+          const int slot = (t * NB + i) % PB;
           if constexpr (WANT_DV) {
             const u32x2 g0 = lds_read_tr(Gs, o0), g1 = lds_read_tr(Gs, o1);
-            dv[e] = mma16<BF16>(u32x4{g0[0], g0[1], g1[0], g1[1]}, pf, dv[e]);
+            bg[slot] = u32x4{g0[0], g0[1], g1[0], g1[1]};
           }
           if constexpr (WANT_DK) {
             const u32x2 q0 = lds_read_tr(Qs, o0), q1 = lds_read_tr(Qs, o1);
-            dk[e] = mma16<BF16>(u32x4{q0[0], q0[1], q1[0], q1[1]}, sf, dk[e]);
+            bq[slot] = u32x4{q0[0], q0[1], q1[0], q1[1]};
+          }
+        };
+        auto b_step = [&](int t, int i) {
+          const int x = i / OB, e = i % OB, slot = (t * NB + i) % PB;
+          if constexpr (WANT_DV) dv[e] = mma16<BF16>(bg[slot], pf[t][x], dv[e]);
+          if constexpr (WANT_DK) dk[e] = mma16<BF16>(bq[slot], sf[t][x], dk[e]);
+        };
+
+        stat_load(0);
+  #pragma unroll
+        for (int kc = 0; kc < PA; ++kc) a_load(0, kc);
+        __builtin_amdgcn_sched_barrier(0);
+        // A0
+  #pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          a_step(0, kc);
+          if (kc + PA < KC) a_load(0, kc + PA);
+          else a_load(1, kc + PA - KC);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        stat_load(1);
+        // A1 + V0
+  #pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          a_step(1, kc);
+          if (kc + PA < KC) a_load(1, kc + PA);
+          else if (kc + PA - KC < PB) b_load(0, kc + PA - KC);
+          v_range(0, kc * 16 / KC, (kc + 1) * 16 / KC);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // the B operands PA .. PB - 1 of block 0 that A1 had no step left to carry
+  #pragma unroll
+        for (int i = (PA < PB ? PA : PB); i < PB; ++i) b_load(0, i);
+        // B0 + V1
+  #pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          b_step(0, i);
+          if (i + PB < NB) b_load(0, i + PB);
+          else b_load(1, i + PB - NB);
+          v_range(1, i * 16 / NB, (i + 1) * 16 / NB);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // B1
+  #pragma unroll
+        for (int i = 0; i < NB; ++i) {
+          b_step(1, i);
+          if (i + PB < NB) b_load(1, i + PB);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+      // d = 64: the simple order (the pipelined one needs more registers than three waves
+      // per SIMD leave, and runs slower there)
+  #pragma unroll
+      for (int t = 0; t < 2; ++t) {  // 32-query blocks of the tile
+        // S = Q K^T and dP = dO V^T for queries 32t + (8(r/4) + 4h + r%4), key l32
+        f32x16 s = {}, dp = {};
+  #pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const int off = qb + tl.rb + 32 * t * C::ROWB + ((32 * kc) ^ tl.rx);
+          s = mma16<BF16>(lds_read16(Qs, off), kf[kc], s);
+          if constexpr (WANT_DK) dp = mma16<BF16>(lds_read16(Gs, off), vf[kc], dp);
+        }
+        // P = 2^(c s - lse2_q), dS = P (dP - D_q); the statistics of queries
+        // 32t + 8g + 4h + 0..3 are one 16-byte broadcast read each
+        float p[16], ds[16];
+  #pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int qo = (32 * t + 8 * g + 4 * h) * 4;
+          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(Ls + st * C::STATB + qo);
+          f32x4 d4 = {};
+          if constexpr (WANT_DK) d4 = *reinterpret_cast<const f32x4 *>(Ds + st * C::STATB + qo);
+  #pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            const int r = 4 * g + s4;
+            p[r] = ex2(fmaf(s[r], c, -l4[s4]));
+            ds[r] = WANT_DK ? p[r] * (dp[r] - d4[s4]) : 0.f;
+          }
+        }
+        // operands of k-steps 2t, 2t + 1: registers 8x .. 8x + 7 hold queries
+        // 16(2t + x) + 8y + 4h + s4 in slot 4y + s4
+  #pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int rb = 8 * x;
+          const u32x4 pf = {pack16<BF16>(p[rb + 0], p[rb + 1]), pack16<BF16>(p[rb + 2], p[rb + 3]),
+                            pack16<BF16>(p[rb + 4], p[rb + 5]), pack16<BF16>(p[rb + 6], p[rb + 7])};
+          const u32x4 sf = {pack16<BF16>(ds[rb + 0], ds[rb + 1]), pack16<BF16>(ds[rb + 2], ds[rb + 3]),
+                            pack16<BF16>(ds[rb + 4], ds[rb + 5]), pack16<BF16>(ds[rb + 6], ds[rb + 7])};
+          const int u = 2 * t + x;
+  #pragma unroll
+          for (int e = 0; e < OB; ++e) {
+            const int o0 = qb + tl.tb0 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
+            const int o1 = qb + tl.tb1 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
+            if constexpr (WANT_DV) {
+              const u32x2 g0 = lds_read_tr(Gs, o0), g1 = lds_read_tr(Gs, o1);
+              dv[e] = mma16<BF16>(u32x4{g0[0], g0[1], g1[0], g1[1]}, pf, dv[e]);
+            }
+            if constexpr (WANT_DK) {
+              const u32x2 q0 = lds_read_tr(Qs, o0), q1 = lds_read_tr(Qs, o1);
+              dk[e] = mma16<BF16>(u32x4{q0[0], q0[1], q1[0], q1[1]}, sf, dk[e]);
+            }
           }
         }
       }
