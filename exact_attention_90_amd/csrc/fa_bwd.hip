@@ -28,6 +28,25 @@
 
 namespace fa {
 
+// LDS reads from an absolute 32-bit LDS byte address.  A dynamic-LDS array's own
+// address is a link-time constant that the compiler adds to every offset with a VALU add;
+// folding it into a lane's address once leaves only immediate offsets at the reads.
+typedef __attribute__((address_space(3))) char lds_byte;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+  return uint32_t(uintptr_t((const lds_byte *)p));
+}
+__device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
+  return *(const lds_u32x4 *)(uintptr_t)addr;
+}
+__device__ __forceinline__ f32x4 lds_read_f32x4_at(uint32_t addr) {
+  return __builtin_bit_cast(f32x4, *(const lds_u32x4 *)(uintptr_t)addr);
+}
+__device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)addr);
+  return __builtin_bit_cast(u32x2, r);
+}
+
 // A streamed tile is read two ways: 16-byte row reads (the A operand of S = Q K^T and
 // dP = dO V^T) and transposing reads (the A operand of dV^T = dO^T P and dK^T = Q^T dS,
 // or of dQ^T = K^T dS^T).  One XOR key per row serves both without bank conflicts: over
@@ -242,6 +261,23 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
   }
 
   const int nqt = (N + C::BT - 1) / C::BT;
+  // LDS addresses of the operand reads in the current stage, one per k-step (row reads)
+  // and per output block (transposing reads); the dO tiles are an immediate offset from
+  // them.  The stages are TILEB (statistics: STATB) apart, so one add per register moves
+  // them to the next tile's stage.
+  const uint32_t q_lds = lds_addr(Qs);
+  uint32_t a_off[KC], b_off0[OB], b_off1[OB];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) a_off[kc] = q_lds + (tl.rb + ((32 * kc) ^ tl.rx));
+#pragma unroll
+  for (int e = 0; e < OB; ++e) {
+    b_off0[e] = q_lds + (tl.tb0 + ((64 * e) ^ tl.tx));
+    b_off1[e] = q_lds + (tl.tb1 + ((64 * e) ^ tl.tx));
+  }
+  // statistics of queries 4h + (8g + 32t): this lane's 16-byte group, stage 0
+  uint32_t stat_off = q_lds + 4 * C::TILEB + 16 * h;
+  constexpr int GS = 2 * C::TILEB;   // dO tile stage - Q tile stage
+  constexpr int DS = 2 * C::STATB;   // D stage - lse2 stage
   load_tile(0, 0);
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   lds_barrier();
@@ -249,7 +285,15 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
     const int st = qt & 1;
     // the other stage held tile qt - 1, released by the barrier that ended it
     if (qt + 1 < nqt) load_tile(st ^ 1, qt + 1);
-    const int qb = st * C::TILEB;
+    // held in registers across the loop rather than recomputed at each read
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) pin(a_off[kc]);
+#pragma unroll
+    for (int e = 0; e < OB; ++e) {
+      pin(b_off0[e]);
+      pin(b_off1[e]);
+    }
+    pin(stat_off);
     if constexpr (D >= 128) {
       // The tile's two 32-query blocks t = 0, 1 go through three parts:
       //   A(t)  S = Q K^T and dP = dO V^T for queries 32t + (8(r/4) + 4h + r%4), key l32
@@ -263,7 +307,7 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
       // step kc is position t KC + kc), so that the next block's first reads never take a
       // slot this block still needs; fences keep every step in place.
       {
-        constexpr int PA = 3, PB = 2, NB = 2 * OB;
+        constexpr int PA = 4, PB = 2, NB = 2 * OB;
         static_assert(PA <= KC && PB <= NB, "prefetch depth within one part");
         f32x16 s[2], dp[2];
         float p[2][16], ds[2][16];
@@ -272,10 +316,10 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
         u32x4 qa[PA], ga[PA], bg[PB], bq[PB];
         // A operands: rows 32t + l32 of the Q and dO tiles at logical chunk 2kc + h
         auto a_load = [&](int t, int kc) {
-          const int off = qb + tl.rb + 32 * t * C::ROWB + ((32 * kc) ^ tl.rx);
+          const uint32_t off = a_off[kc] + 32 * t * C::ROWB;
           const int slot = (t * KC + kc) % PA;
-          qa[slot] = lds_read16(Qs, off);
-          if constexpr (WANT_DK) ga[slot] = lds_read16(Gs, off);
+          qa[slot] = lds_read16_at(off);
+          if constexpr (WANT_DK) ga[slot] = lds_read16_at(off + GS);
         };
         auto a_step = [&](int t, int kc) {
           const int slot = (t * KC + kc) % PA;
@@ -286,9 +330,9 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
         auto stat_load = [&](int t) {
   #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int qo = st * C::STATB + (32 * t + 8 * g + 4 * h) * 4;
-            lq[t][g] = *reinterpret_cast<const f32x4 *>(Ls + qo);
-            if constexpr (WANT_DK) dq4[t][g] = *reinterpret_cast<const f32x4 *>(Ds + qo);
+            const uint32_t qo = stat_off + (32 * t + 8 * g) * 4;
+            lq[t][g] = lds_read_f32x4_at(qo);
+            if constexpr (WANT_DK) dq4[t][g] = lds_read_f32x4_at(qo + DS);
           }
         };
         // V(t) for registers lo .. hi-1; operand block x (registers 8x .. 8x + 7: queries
@@ -297,8 +341,14 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
   #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (r >= lo && r < hi) {
-              p[t][r] = ex2(fmaf(s[t][r], c, -lq[t][r >> 2][r & 3]));
-              ds[t][r] = WANT_DK ? p[t][r] * (dp[t][r] - dq4[t][r >> 2][r & 3]) : 0.f;
+              // taken into vector registers at this step (left alone, the compiler moves
+              // the whole block's vector work up to where its products end, where no
+              // matrix-core step runs beside it)
+              float sv = s[t][r], gv = WANT_DK ? dp[t][r] : 0.f;
+              pin(sv);
+              if constexpr (WANT_DK) pin(gv);
+              p[t][r] = ex2(fmaf(sv, c, -lq[t][r >> 2][r & 3]));
+              ds[t][r] = WANT_DK ? p[t][r] * (gv - dq4[t][r >> 2][r & 3]) : 0.f;
             }
   #pragma unroll
           for (int x = 0; x < 2; ++x)
@@ -314,15 +364,15 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
         // B step i of block t: k-step u = 2t + i / OB (16 queries), output block e = i % OB
         auto b_load = [&](int t, int i) {
           const int u = 2 * t + i / OB, e = i % OB;
-          const int o0 = qb + tl.tb0 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
-          const int o1 = qb + tl.tb1 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
+          const uint32_t o0 = b_off0[e] + 16 * u * C::ROWB;
+          const uint32_t o1 = b_off1[e] + 16 * u * C::ROWB;
           const int slot = (t * NB + i) % PB;
           if constexpr (WANT_DV) {
-            const u32x2 g0 = lds_read_tr(Gs, o0), g1 = lds_read_tr(Gs, o1);
+            const u32x2 g0 = lds_read_tr_at(o0 + GS), g1 = lds_read_tr_at(o1 + GS);
             bg[slot] = u32x4{g0[0], g0[1], g1[0], g1[1]};
           }
           if constexpr (WANT_DK) {
-            const u32x2 q0 = lds_read_tr(Qs, o0), q1 = lds_read_tr(Qs, o1);
+            const u32x2 q0 = lds_read_tr_at(o0), q1 = lds_read_tr_at(o1);
             bq[slot] = u32x4{q0[0], q0[1], q1[0], q1[1]};
           }
         };
@@ -383,19 +433,19 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
         f32x16 s = {}, dp = {};
   #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const int off = qb + tl.rb + 32 * t * C::ROWB + ((32 * kc) ^ tl.rx);
-          s = mma16<BF16>(lds_read16(Qs, off), kf[kc], s);
-          if constexpr (WANT_DK) dp = mma16<BF16>(lds_read16(Gs, off), vf[kc], dp);
+          const uint32_t off = a_off[kc] + 32 * t * C::ROWB;
+          s = mma16<BF16>(lds_read16_at(off), kf[kc], s);
+          if constexpr (WANT_DK) dp = mma16<BF16>(lds_read16_at(off + GS), vf[kc], dp);
         }
         // P = 2^(c s - lse2_q), dS = P (dP - D_q); the statistics of queries
         // 32t + 8g + 4h + 0..3 are one 16-byte broadcast read each
         float p[16], ds[16];
   #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int qo = (32 * t + 8 * g + 4 * h) * 4;
-          const f32x4 l4 = *reinterpret_cast<const f32x4 *>(Ls + st * C::STATB + qo);
+          const uint32_t qo = stat_off + (32 * t + 8 * g) * 4;
+          const f32x4 l4 = lds_read_f32x4_at(qo);
           f32x4 d4 = {};
-          if constexpr (WANT_DK) d4 = *reinterpret_cast<const f32x4 *>(Ds + st * C::STATB + qo);
+          if constexpr (WANT_DK) d4 = lds_read_f32x4_at(qo + DS);
   #pragma unroll
           for (int s4 = 0; s4 < 4; ++s4) {
             const int r = 4 * g + s4;
@@ -415,20 +465,29 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
           const int u = 2 * t + x;
   #pragma unroll
           for (int e = 0; e < OB; ++e) {
-            const int o0 = qb + tl.tb0 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
-            const int o1 = qb + tl.tb1 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
+            const uint32_t o0 = b_off0[e] + 16 * u * C::ROWB;
+            const uint32_t o1 = b_off1[e] + 16 * u * C::ROWB;
             if constexpr (WANT_DV) {
-              const u32x2 g0 = lds_read_tr(Gs, o0), g1 = lds_read_tr(Gs, o1);
+              const u32x2 g0 = lds_read_tr_at(o0 + GS), g1 = lds_read_tr_at(o1 + GS);
               dv[e] = mma16<BF16>(u32x4{g0[0], g0[1], g1[0], g1[1]}, pf, dv[e]);
             }
             if constexpr (WANT_DK) {
-              const u32x2 q0 = lds_read_tr(Qs, o0), q1 = lds_read_tr(Qs, o1);
+              const u32x2 q0 = lds_read_tr_at(o0), q1 = lds_read_tr_at(o1);
               dk[e] = mma16<BF16>(u32x4{q0[0], q0[1], q1[0], q1[1]}, sf, dk[e]);
             }
           }
         }
       }
     }
+    const int flip = st ? -C::TILEB : C::TILEB;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) a_off[kc] += flip;
+#pragma unroll
+    for (int e = 0; e < OB; ++e) {
+      b_off0[e] += flip;
+      b_off1[e] += flip;
+    }
+    stat_off += st ? -C::STATB : C::STATB;
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));  // tile qt + 1 has landed
     lds_barrier();
   }
