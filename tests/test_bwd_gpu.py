@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
+from synth.configs import HEADDIM_WORKLOADS, WORKLOADS
 from synth.inputs import make_dout, make_qkv, quantize
 from tests.gpu_util import say, to_device
 
@@ -164,3 +165,33 @@ def test_bwd_larger_sampled_heads():
     assert_grads(sel, ref, dtype, "B2H8N2048 heads 0,15")
     for a in gpu:
         assert np.isfinite(a).all()
+
+
+@pytest.mark.parametrize("name", ["c3", "d256"])
+def test_bwd_workload_full_size_sampled(name):
+    # the benchmark's launch at full size (same inputs, dO and scale as bench.py --pass
+    # bwd); every gradient of three whole heads (first, one inside, last) against the
+    # oracle, and all of dQ, dK, dV finite
+    import torch
+
+    import exact_attention_90_amd as fa
+
+    w = WORKLOADS[name] if name in WORKLOADS else HEADDIM_WORKLOADS[name]
+    scale = float(np.float32(w.scale))
+    say(f"bwd {name}: generating {w.short()}")
+    x = make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.mult)
+    g_np = make_dout(w.B, w.H, w.N, w.d, w.seed + 5000)
+    xd = to_device(x, w.dtype)
+    o, lse = fa.fwd(xd["q"], xd["k"], xd["v"], scale)
+    g = torch.from_numpy(g_np).to("cuda")
+    say(f"bwd {name}: fused backward")
+    grads = fa.bwd(xd["q"], xd["k"], xd["v"], o, lse, g, scale)
+    torch.cuda.synchronize()
+    heads = [0, (w.B * w.H) // 2 + 1, w.B * w.H - 1]
+    idx = torch.tensor(heads, device="cuda")
+    sel = [t.reshape(w.B * w.H, w.N, w.d).index_select(0, idx).cpu().numpy() for t in grads]
+    for t in grads:
+        assert bool(torch.isfinite(t).all())
+    say(f"bwd {name}: oracle on heads {heads}")
+    ref = oracle.attention_bwd(x["q"], x["k"], x["v"], g_np, w.dtype, scale, heads=heads)
+    assert_grads(sel, ref, w.dtype, f"{name} heads {heads}")
