@@ -204,6 +204,10 @@ def main() -> int:
                     help="fwd: the forward pass (the headline); bwd: the backward pass "
                          "(fa_bwd), counted as five N x N x d products (10 B H N^2 d flops)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--zero-inputs", action="store_true",
+                    help="diagnostic: all-zero Q, K, V of the workload's shape instead of the "
+                         "seeded N(0,1) draw (same instructions and memory traffic, no data "
+                         "toggling; contrasts the power-limited clock with the unlimited one)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run device-to-device copies of MIB MiB (a "
@@ -240,6 +244,8 @@ def main() -> int:
     scale32 = float(np.float32(w.scale))
     print(f"[bench] generating {w.name}: {w.short()}", file=sys.stderr, flush=True)
     x = make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.mult)
+    if args.zero_inputs:
+        x = {n: np.zeros_like(a) for n, a in x.items()}
     dev = torch.device("cuda:0")
     q, k, v = (to_torch(x[n], w.dtype).to(dev) for n in ("q", "k", "v"))
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
@@ -288,8 +294,9 @@ def main() -> int:
         traffic = rec.get("bytes_per_launch")
 
     line = {
-        "metric": METRIC if w.name == "c3" and args.path == "fused" else
-        f"fwd attention TFLOP/s ({args.path}), {w.short()}",
+        "metric": (METRIC if w.name == "c3" and args.path == "fused" else
+                   f"fwd attention TFLOP/s ({args.path}), {w.short()}")
+        + (" [all-zero inputs: power diagnostic]" if args.zero_inputs else ""),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -300,7 +307,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic",
+        "data": "synthetic, all zeros" if args.zero_inputs else "synthetic",
         "config": {
             "workload": f"{w.name}: non-causal attention forward, {w.short()}, "
                         f"scale 1/sqrt({w.d}), O fp32 + LSE",
