@@ -378,6 +378,8 @@ def bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev):
               file=sys.stderr)
         return 2
     g_np = make_dout(w.B, w.H, w.N, w.d, w.seed + 5000)
+    if args.zero_inputs:
+        g_np = g_np * 0
     g = torch.from_numpy(g_np).to(dev)
     fa.fwd(q, k, v, scale32, out=o, lse=lse)
     ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8,
@@ -405,10 +407,12 @@ def bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev):
     peak = PEAK_TFLOPS[w.dtype]
     rec = committed_traffic(w.name, "bwd")
     line = {
-        "metric": f"bwd attention TFLOP/s (5 products, 10 B H N^2 d), {w.short()}",
+        "metric": f"bwd attention TFLOP/s (5 products, 10 B H N^2 d), {w.short()}"
+        + (" [all-zero inputs: power diagnostic]" if args.zero_inputs else ""),
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic, all zeros" if args.zero_inputs else "synthetic",
         "config": {"workload": f"{w.name}: attention backward (dQ, dK, dV from O, LSE, dO), "
                                f"{w.short()}, scale 1/sqrt({w.d})",
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "path": "fused",
