@@ -200,6 +200,9 @@ def main() -> int:
     ap.add_argument("--shape", default=None, metavar="B,H,N,d,dtype",
                     help="measure an ad-hoc shape instead of a named workload (N(0,1) inputs)")
     ap.add_argument("--path", default="fused", choices=["fused", "naive"])
+    ap.add_argument("--split", type=int, default=0, metavar="S",
+                    help="fused path through fa_fwd_split with S key ranges per head "
+                         "(for few heads and long sequences); 0 = fa_fwd")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="fwd: the forward pass (the headline); bwd: the backward pass "
                          "(fa_bwd), counted as five N x N x d products (10 B H N^2 d flops)")
@@ -253,13 +256,21 @@ def main() -> int:
     if args.which == "bwd":
         return bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev)
     ws = None
+    if args.split:
+        if args.path != "fused" or w.dtype == "f32":
+            print("bench.py: --split runs the fused path on 16-bit inputs", file=sys.stderr)
+            return 2
+        ws = torch.empty(fa.split_workspace_bytes(w.B, w.H, w.N, w.d, args.split),
+                         dtype=torch.uint8, device=dev)
     if args.path == "naive":
         nb = fa.naive_workspace_bytes(w.B, w.H, w.N, q.dtype)
         ws = (torch.empty(nb, dtype=torch.uint8, device=dev),
               torch.empty(nb, dtype=torch.uint8, device=dev))
 
     def step():
-        if args.path == "fused":
+        if args.split:
+            fa.fwd_split(q, k, v, args.split, scale32, out=o, lse=lse, workspace=ws)
+        elif args.path == "fused":
             fa.fwd(q, k, v, scale32, out=o, lse=lse)
         else:
             fa.naive_fwd(q, k, v, scale32, out=o, lse=lse, workspace=ws)
@@ -294,8 +305,9 @@ def main() -> int:
         traffic = rec.get("bytes_per_launch")
 
     line = {
-        "metric": (METRIC if w.name == "c3" and args.path == "fused" else
-                   f"fwd attention TFLOP/s ({args.path}), {w.short()}")
+        "metric": (METRIC if w.name == "c3" and args.path == "fused" and not args.split else
+                   f"fwd attention TFLOP/s ({args.path}"
+                   + (f", {args.split} key ranges merged" if args.split else "") + f"), {w.short()}")
         + (" [all-zero inputs: power diagnostic]" if args.zero_inputs else ""),
         "value": round(value, 3),
         "unit": "TFLOP/s",
@@ -311,7 +323,7 @@ def main() -> int:
         "config": {
             "workload": f"{w.name}: non-causal attention forward, {w.short()}, "
                         f"scale 1/sqrt({w.d}), O fp32 + LSE",
-            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "path": args.path,
+            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "path": args.path, "key_ranges": args.split or 1,
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100.0 * value / peak, 2),

@@ -4,6 +4,8 @@ PyTorch supplies device memory and the stream; every step of the computation run
 in the library's HIP kernels.  The function names follow the C boundary:
 
     fwd(q, k, v, scale=None)        -> (o, lse)   fused FlashAttention forward
+    fwd_split(q, k, v, nsplit)      -> (o, lse)   the same with each head's keys cut into
+                                                  nsplit ranges and merged (few heads)
     naive_fwd(q, k, v, scale=None)  -> (o, lse)   materialised S/P contrast path
     bwd(q, k, v, o, lse, dout)      -> (dq, dk, dv)  backward pass (recomputes P)
 
@@ -71,6 +73,33 @@ def fwd(q, k, v, scale: float | None = None, out=None, lse=None, stream=None):
     rc = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
                     H, N, d, scale, _CODES[q.dtype], _stream(q, stream))
     _lib.check(rc, "fa_fwd")
+    return out, lse
+
+
+def split_workspace_bytes(B: int, H: int, N: int, d: int, nsplit: int) -> int:
+    return int(_lib.load().fa_fwd_split_workspace_bytes(B, H, N, d, nsplit))
+
+
+def fwd_split(q, k, v, nsplit: int, scale: float | None = None, out=None, lse=None,
+              workspace=None, stream=None):
+    """Key-split fused forward (16-bit inputs): returns (o, lse), equal to fwd()'s within
+    rounding.  workspace: optional uint8 device tensor of at least
+    split_workspace_bytes(B, H, N, d, nsplit) bytes, 256-byte aligned (allocated when
+    omitted)."""
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q, out, lse)
+    nbytes = split_workspace_bytes(B, H, N, d, nsplit)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("split workspace too small")
+    lib = _lib.load()
+    rc = lib.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), workspace.data_ptr(), int(nsplit), B, H, N, d, scale,
+                          _CODES[q.dtype], _stream(q, stream))
+    _lib.check(rc, "fa_fwd_split")
     return out, lse
 
 

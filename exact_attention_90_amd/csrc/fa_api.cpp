@@ -88,6 +88,56 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
                                      static_cast<hipStream_t>(stream)));
 }
 
+// Workspace of the key-split forward: nsplit slots of partial O (B H N d floats), then
+// nsplit slots of partial LSE (B H N floats), each part starting on a 256-byte boundary.
+namespace {
+struct SplitLayout {
+  unsigned __int128 lse, total;
+};
+SplitLayout split_layout(int B, int H, int N, int d, int nsplit) {
+  const unsigned __int128 rows =
+      (unsigned __int128)(uint64_t)B * (uint64_t)H * (uint64_t)N * (uint64_t)nsplit;
+  SplitLayout L;
+  L.lse = (rows * (uint64_t)d * 4 + 255) / 256 * 256;
+  L.total = L.lse + (rows * 4 + 255) / 256 * 256;
+  return L;
+}
+}  // namespace
+
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int nsplit) {
+  if (B < 0 || H < 0 || N < 0 || nsplit < 1 || nsplit > FA_MAX_SPLIT) return 0;
+  if (d != 64 && d != 128 && d != 256) return 0;
+  const unsigned __int128 t = split_layout(B, H, N, d, nsplit).total;
+  if (t > (unsigned __int128)std::numeric_limits<size_t>::max())
+    return std::numeric_limits<size_t>::max();
+  return (size_t)t;
+}
+
+int fa_fwd_split(const void *q, const void *k, const void *v, float *o, float *lse,
+                 void *workspace, int nsplit, int B, int H, int N, int d, float scale, int dtype,
+                 void *stream) {
+  bool empty = false;
+  int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
+  if (rc != FA_OK) return rc;
+  if (dtype == FA_F32) return FA_ERR_DTYPE;
+  if (nsplit < 1 || nsplit > FA_MAX_SPLIT) return FA_ERR_SHAPE;
+  if (empty) return FA_OK;
+  if (!workspace || !aligned(workspace, 256)) return FA_ERR_WORKSPACE;
+  // ranges of whole 64-key tiles; ranges that would start past N are dropped
+  const int tiles = (N + 63) / 64;
+  const int kps = (tiles + nsplit - 1) / nsplit * 64;
+  const int used = (N + kps - 1) / kps;
+  const int64_t qtiles = (int64_t(N) + fa::kFusedBM - 1) / fa::kFusedBM;
+  if (int64_t(B) * H * qtiles * used > fa::kMaxGrid) return FA_ERR_SHAPE;
+  rc = device_ready();
+  if (rc != FA_OK) return rc;
+  const SplitLayout L = split_layout(B, H, N, d, nsplit);
+  char *ws = static_cast<char *>(workspace);
+  return hip_status(fa::launch_fused_split(
+      make_problem(q, k, v, o, lse, B, H, N, d, scale, dtype), reinterpret_cast<float *>(ws),
+      reinterpret_cast<float *>(ws + (size_t)L.lse), used, kps, static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype) {
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16) return 0;
   if (B < 0 || H < 0 || N < 0) return 0;

@@ -64,7 +64,7 @@ template <int D, bool BF16, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES>::WPE)) void fa_fwd16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int N,
-    int nqt, int G, float c) {
+    int nqt, int G, float c, int nsplit, int kps) {
   using C = Cfg16<D, WAVES>;
   constexpr int SB = C::SB, OB = C::OB, PU = C::PU, CPT = C::CPT;
   constexpr int NA = SB * C::KC;  // matrix-core steps of S^T = K Q^T per tile
@@ -77,14 +77,22 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES>::WPE)) void fa_fwd16_k
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
+  // workgroup L: Q tile L % nqt of key range (L / nqt) % nsplit of head L / (nqt nsplit).
+  // Key range g holds keys [g kps, min(N, (g + 1) kps)); its result (O normalised over
+  // those keys, and their LSE) goes to slot g of O and LSE, whose slots are B H N d and
+  // B H N values apart.  With nsplit = 1 (kps = N) that is the whole attention.
   const int L = xcd_remap(blockIdx.x, G);
-  const int bh = L / nqt, q0 = (L % nqt) * C::BM;
+  const int qt = L % nqt, kg = (L / nqt) % nsplit, bh = L / nqt / nsplit;
+  const int q0 = qt * C::BM;
   const int64_t hoff = int64_t(bh) * N * D;
-  // buffer resources over this head's [N, D] slices: loads past row N - 1 read zeros
+  const int64_t bhn = int64_t(G / (nqt * nsplit)) * N;  // rows of one output slot
+  const int kbeg = kg * kps, NK = min(N - kbeg, kps);    // keys of this range, >= 1
+  // buffer resources over this head's [N, D] slices (K and V: the range's rows): loads
+  // past the last row read zeros
   const uint32_t head_bytes = uint32_t(N) * C::ROWB;
   const auto qrs = make_rsrc(Q + hoff, head_bytes);
-  const auto krs = make_rsrc(K + hoff, head_bytes);
-  const auto vrs = make_rsrc(V + hoff, head_bytes);
+  const auto krs = make_rsrc(K + hoff + int64_t(kbeg) * D, uint32_t(NK) * C::ROWB);
+  const auto vrs = make_rsrc(V + hoff + int64_t(kbeg) * D, uint32_t(NK) * C::ROWB);
   constexpr int ST_STEP = C::NT * 16;  // bytes between a thread's chunks, in LDS and memory
   // A tile of rows is one contiguous block of global memory: thread tid moves the
   // 16-byte chunks tid + NT i.  Their LDS rows differ by NT/CPR per i, which leaves
@@ -190,8 +198,8 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES>::WPE)) void fa_fwd16_k
   // alpha and P row sum; lazy form only: the partial sums of P as rounded to binary16
   // for the P V product (lp, and rp for the pending tile)
   float mc = -INFINITY, l = 0.f, alpha = 0.f, rs = 0.f, lp = 0.f, rp = 0.f;
-  const int nkt = (N + C::BN - 1) / C::BN;
-  const int nlast = N - (nkt - 1) * C::BN;  // valid keys of the last tile, 1 .. BN
+  const int nkt = (NK + C::BN - 1) / C::BN;
+  const int nlast = NK - (nkt - 1) * C::BN;  // valid keys of the last tile, 1 .. BN
 
   // ---- the softmax of one tile is split across the two halves of an iteration ----
   // S^T holds 32 scores per lane: block 0 (keys 0-31 of the tile, registers s[0]) and
@@ -444,8 +452,8 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES>::WPE)) void fa_fwd16_k
   constexpr int NHALF = (32 * D * 4 + WAVE_LDS - 1) / WAVE_LDS;
   const int row0 = q0 + 32 * w;  // the wave's first query row
   store_rows_lds<D, NHALF>(o, mc, l, LAZY ? lp : l, smem + w * WAVE_LDS,
-                           O + hoff + int64_t(row0) * D, LSE + int64_t(bh) * N + row0, lane,
-                           N - row0);
+                           O + kg * bhn * D + hoff + int64_t(row0) * D,
+                           LSE + kg * bhn + int64_t(bh) * N + row0, lane, N - row0);
 }
 
 // ====================================================================================
@@ -619,20 +627,31 @@ static hipError_t allow_lds(KernelT kernel, int bytes) {
 template <int D>
 constexpr int waves16() { return D == 128 ? 8 : 4; }
 
+// nsplit key ranges of kps keys each (the last may be shorter, none is empty); with
+// nsplit = 1 and kps = N the kernel writes the attention itself to o and lse
 template <int D, bool BF16, int WAVES = waves16<D>()>
-static hipError_t run16(const Problem &p, hipStream_t stream) {
+static hipError_t run16(const Problem &p, float *o, float *lse, int nsplit, int kps,
+                        hipStream_t stream) {
   using C = Cfg16<D, WAVES>;
   auto kern = fa_fwd16_kernel<D, BF16, WAVES>;
   // raise the dynamic-LDS cap once; a refusal surfaces as a launch error below
   static const hipError_t attr = allow_lds(kern, C::LDS);
   (void)attr;
   const int nqt = (p.N + C::BM - 1) / C::BM;
-  const int G = nqt * p.B * p.H;
+  const int G = nqt * p.B * p.H * nsplit;
   const float c = p.scale * kLog2e;
   hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
                      static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
-                     static_cast<const uint16_t *>(p.v), p.o, p.lse, p.N, nqt, G, c);
+                     static_cast<const uint16_t *>(p.v), o, lse, p.N, nqt, G, c, nsplit, kps);
   return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t run16_any(const Problem &p, float *o, float *lse, int nsplit, int kps,
+                            hipStream_t stream) {
+  return p.d == 256 ? run16<256, BF16>(p, o, lse, nsplit, kps, stream)
+         : p.d == 128 ? run16<128, BF16>(p, o, lse, nsplit, kps, stream)
+                      : run16<64, BF16>(p, o, lse, nsplit, kps, stream);
 }
 
 template <int D>
@@ -654,18 +673,72 @@ static hipError_t run32(const Problem &p, hipStream_t stream) {
 hipError_t launch_fused(const Problem &p, hipStream_t stream) {
   switch (p.dtype) {
     case kF16:
-      return p.d == 256 ? run16<256, false>(p, stream)
-             : p.d == 128 ? run16<128, false>(p, stream)
-                          : run16<64, false>(p, stream);
+      return run16_any<false>(p, p.o, p.lse, 1, p.N, stream);
     case kBF16:
-      return p.d == 256 ? run16<256, true>(p, stream)
-             : p.d == 128 ? run16<128, true>(p, stream)
-                          : run16<64, true>(p, stream);
+      return run16_any<true>(p, p.o, p.lse, 1, p.N, stream);
     default:
       return p.d == 256 ? run32<256>(p, stream)
              : p.d == 128 ? run32<128>(p, stream)
                           : run32<64>(p, stream);
   }
+}
+
+// ------------------------------------------------------------------------------------
+// Key-split forward.  The keys of every head are cut into ranges of kps keys; one
+// launch of the fused kernel computes, for each range g, the attention of every query
+// row over that range alone (O_g, normalised by its own row sum, and LSE_g), and the
+// merge kernel combines the ranges with the block-merge rule of the Triton tutorial
+// (section 2.3) and the MUSA guide's block update (step e):
+//   LSE = log sum_g exp(LSE_g),   O = sum_g exp(LSE_g - LSE) O_g,
+// evaluated against M = max_g LSE_g for range safety.  Rows are independent; each
+// thread owns 4 columns of one row.
+template <int D>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const float *__restrict__ Opart,
+                                                       const float *__restrict__ Lpart,
+                                                       float *__restrict__ O,
+                                                       float *__restrict__ LSE, int64_t rows,
+                                                       int nsplit) {
+  constexpr int TPR = D / 4;      // threads per row
+  constexpr int RPB = 256 / TPR;  // rows per workgroup
+  const int64_t row = int64_t(blockIdx.x) * RPB + threadIdx.x / TPR;
+  const int col = 4 * (threadIdx.x % TPR);
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int g = 0; g < nsplit; ++g) m = fmaxf(m, Lpart[g * rows + row]);
+  float wsum = 0.f, a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int g = 0; g < nsplit; ++g) {
+    const float wg = expf(Lpart[g * rows + row] - m);
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(Opart + (g * rows + row) * D + col);
+    wsum += wg;
+    a0 = fmaf(wg, v[0], a0);
+    a1 = fmaf(wg, v[1], a1);
+    a2 = fmaf(wg, v[2], a2);
+    a3 = fmaf(wg, v[3], a3);
+  }
+  const float inv = 1.0f / wsum;
+  *reinterpret_cast<f32x4 *>(O + row * D + col) = f32x4{a0 * inv, a1 * inv, a2 * inv, a3 * inv};
+  if (col == 0) LSE[row] = m + logf(wsum);
+}
+
+template <int D>
+static hipError_t run_merge(const Problem &p, const float *opart, const float *lpart,
+                            int nsplit, hipStream_t stream) {
+  constexpr int RPB = 256 / (D / 4);
+  const int64_t rows = int64_t(p.B) * p.H * p.N;
+  const int64_t blocks = (rows + RPB - 1) / RPB;
+  hipLaunchKernelGGL(fa_merge_kernel<D>, dim3(unsigned(blocks)), dim3(256), 0, stream, opart,
+                     lpart, p.o, p.lse, rows, nsplit);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_split(const Problem &p, float *opart, float *lpart, int nsplit,
+                              int kps, hipStream_t stream) {
+  hipError_t e = p.dtype == kBF16 ? run16_any<true>(p, opart, lpart, nsplit, kps, stream)
+                                  : run16_any<false>(p, opart, lpart, nsplit, kps, stream);
+  if (e != hipSuccess) return e;
+  return p.d == 256 ? run_merge<256>(p, opart, lpart, nsplit, stream)
+         : p.d == 128 ? run_merge<128>(p, opart, lpart, nsplit, stream)
+                      : run_merge<64>(p, opart, lpart, nsplit, stream);
 }
 
 }  // namespace fa

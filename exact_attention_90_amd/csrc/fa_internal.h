@@ -41,6 +41,10 @@ struct BwdProblem {
 };
 
 hipError_t launch_fused(const Problem &p, hipStream_t stream);
+// 16-bit inputs: nsplit key ranges of kps keys into the partial buffers (opart: nsplit
+// slots of B H N d floats, lpart: nsplit slots of B H N floats), then merged into p.o, p.lse
+hipError_t launch_fused_split(const Problem &p, float *opart, float *lpart, int nsplit,
+                              int kps, hipStream_t stream);
 hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream);    // every dtype
 hipError_t launch_bwd32(const BwdProblem &p, hipStream_t stream);  // fp32 inputs
 hipError_t launch_naive(const Problem &p, void *s_ws, void *p_ws, hipStream_t stream);

@@ -92,6 +92,50 @@ enum fa_status {
 int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int N,
            int d, float scale, int dtype, void *stream);
 
+/* Largest number of key ranges fa_fwd_split accepts. */
+#define FA_MAX_SPLIT 64
+
+/*
+ * fa_fwd_split - fa_fwd with the keys of every head cut into ranges, for shapes
+ * with few heads and long sequences (B*H*ceil(N/256) well below the number of
+ * compute units), where one workgroup per Q tile leaves the device idle.
+ *
+ * The keys are cut into nsplit ranges of whole 64-key tiles (ceil(ceil(N/64) /
+ * nsplit) tiles each; ranges that would start at or past N are dropped, so fewer
+ * than nsplit may run).  For each range g the fused kernel computes every query
+ * row's attention over that range alone: O_g (normalised by the range's own row
+ * sum) and LSE_g.  A second kernel merges the ranges with the block-merge rule of
+ * the Triton tutorial (section 2.3, "split K/V, rescale and add"), which is the
+ * online-softmax block update of the MUSA guide (step e) applied to whole blocks:
+ *     LSE = log sum_g exp(LSE_g),     O = sum_g exp(LSE_g - LSE) O_g.
+ * The same rule combines the partial results of a sequence split across GPUs.
+ *
+ *   q, k, v, o, lse, B, H, N, d, scale, stream   as for fa_fwd.
+ *   dtype      FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_DTYPE).
+ *   nsplit     1 .. FA_MAX_SPLIT (else FA_ERR_SHAPE).  nsplit = 1 gives results
+ *              bitwise equal to fa_fwd's.
+ *   workspace  caller-owned device memory of fa_fwd_split_workspace_bytes(B, H, N,
+ *              d, nsplit) bytes, 256-byte aligned (else FA_ERR_WORKSPACE): the
+ *              partial O_g (float32, nsplit x [B, H, N, d]) and LSE_g (float32,
+ *              nsplit x [B, H, N]).  Its contents on entry do not matter; it must
+ *              not be used by other work on the device until the call completes.
+ *
+ * Precision as for fa_fwd; the merge adds one float32 exp and multiply-add per
+ * range and element.  Results are bitwise identical from run to run.
+ * Returns FA_OK or an fa_status error code.
+ */
+int fa_fwd_split(const void *q, const void *k, const void *v, float *o, float *lse,
+                 void *workspace, int nsplit, int B, int H, int N, int d, float scale, int dtype,
+                 void *stream);
+
+/*
+ * Workspace bytes fa_fwd_split needs for these sizes: nsplit * B * H * N * (d + 1)
+ * float32 values, each of the two parts rounded up to 256 bytes.  0 for negative
+ * sizes, d not in {64, 128, 256} or nsplit outside 1 .. FA_MAX_SPLIT; SIZE_MAX if
+ * the size does not fit a size_t.
+ */
+size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int nsplit);
+
 /*
  * fa_naive_fwd - the materialised three-kernel contrast path (not for production).
  *

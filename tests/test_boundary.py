@@ -134,6 +134,35 @@ def test_naive_rejects_bad_workspace(lib):
     assert lib.fa_naive_fwd(*args, None, None, 1, 1, 0, 64, 0.125, 1, None) == 0
 
 
+def split_call(lib, ws=0x8000, nsplit=4, dtype=1, d=64, N=128, B=1, H=1, q=A):
+    return lib.fa_fwd_split(q, B_, C_, O_, L_, ws, nsplit, B, H, N, d, 0.125, dtype, None)
+
+
+def test_split_rejects_bad_arguments(lib):
+    assert split_call(lib, dtype=0) == 4        # fp32 inputs: no key-split path
+    assert split_call(lib, dtype=5) == 4
+    assert split_call(lib, d=96) == 3
+    assert split_call(lib, nsplit=0) == 2
+    assert split_call(lib, nsplit=65) == 2      # beyond FA_MAX_SPLIT
+    assert split_call(lib, ws=0) == 7           # NULL workspace
+    assert split_call(lib, ws=0x8010) == 7      # workspace not 256-byte aligned
+    assert split_call(lib, q=A + 8) == 6
+    assert split_call(lib, B=2**20, H=2**10, N=2**12, nsplit=1) == 2   # grid limit
+    assert split_call(lib, N=0, ws=0) == 0      # empty problem: nothing to launch
+
+
+def test_split_workspace_bytes(lib):
+    # nsplit slots of partial O (d floats per row) and of partial LSE (one float per row),
+    # each part rounded up to 256 bytes
+    assert lib.fa_fwd_split_workspace_bytes(1, 16, 16384, 128, 4) == 4 * 16 * 16384 * 129 * 4
+    assert lib.fa_fwd_split_workspace_bytes(1, 1, 3, 64, 2) == 1536 + 256
+    assert lib.fa_fwd_split_workspace_bytes(1, 1, 3, 64, 0) == 0
+    assert lib.fa_fwd_split_workspace_bytes(1, 1, 3, 64, 65) == 0
+    assert lib.fa_fwd_split_workspace_bytes(1, 1, 3, 96, 2) == 0
+    assert lib.fa_fwd_split_workspace_bytes(-1, 1, 3, 64, 2) == 0
+    assert lib.fa_fwd_split_workspace_bytes(0, 1, 3, 64, 2) == 0
+
+
 def _gpu_present():
     return os.path.exists("/dev/kfd")
 
