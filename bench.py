@@ -254,6 +254,9 @@ def main() -> int:
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     if args.which == "bwd":
+        if args.split:
+            print("bench.py: --split applies to the forward pass only", file=sys.stderr)
+            return 2
         return bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev)
     ws = None
     if args.split:
