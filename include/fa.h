@@ -104,8 +104,8 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
  * nsplit) tiles each; ranges that would start at or past N are dropped, so fewer
  * than nsplit may run).  For each range g the fused kernel computes every query
  * row's attention over that range alone: O_g (normalised by the range's own row
- * sum) and LSE_g.  A second kernel merges the ranges with the block-merge rule of
- * the Triton tutorial (section 2.3, "split K/V, rescale and add"), which is the
+ * sum) and LSE_g.  A second kernel merges the ranges with the two-block update of
+ * normalised partial outputs in the Triton tutorial (section 2.3), which is the
  * online-softmax block update of the MUSA guide (step e) applied to whole blocks:
  *     LSE = log sum_g exp(LSE_g),     O = sum_g exp(LSE_g - LSE) O_g.
  * The same rule combines the partial results of a sequence split across GPUs.
