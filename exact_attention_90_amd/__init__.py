@@ -4,8 +4,8 @@ A C-ABI library (libfa.so, declared in include/fa.h) of hand-written HIP kernels
 plus a thin Python binding.  See ``api`` for the entry points.
 """
 from .api import (bwd, bwd_workspace_bytes, fwd, fwd_split, naive_fwd,  # noqa: F401
-                  naive_workspace_bytes, split_workspace_bytes, version)
+                  naive_workspace_bytes, split_suggest, split_workspace_bytes, version)
 from ._lib import FAError  # noqa: F401
 
-__all__ = ["fwd", "fwd_split", "split_workspace_bytes", "bwd", "bwd_workspace_bytes", "naive_fwd",
+__all__ = ["fwd", "fwd_split", "split_suggest", "split_workspace_bytes", "bwd", "bwd_workspace_bytes", "naive_fwd",
            "naive_workspace_bytes", "version", "FAError"]

@@ -23,7 +23,7 @@ STATUS = {
     8: "FA_ERR_HIP",
 }
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_split_workspace_bytes", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes",
+EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_split_suggest", "fa_fwd_split_workspace_bytes", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes",
            "fa_status_string", "fa_version", "fa_last_hip_error")
 
 _lib = None
@@ -50,6 +50,8 @@ def load():
     lib.fa_fwd.restype = I
     lib.fa_fwd_split.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.fa_fwd_split.restype = I
+    lib.fa_fwd_split_suggest.argtypes = [I, I, I, I, I]
+    lib.fa_fwd_split_suggest.restype = I
     lib.fa_fwd_split_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_fwd_split_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_naive_fwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P]

@@ -4,7 +4,7 @@ PyTorch supplies device memory and the stream; every step of the computation run
 in the library's HIP kernels.  The function names follow the C boundary:
 
     fwd(q, k, v, scale=None)        -> (o, lse)   fused FlashAttention forward
-    fwd_split(q, k, v, nsplit)      -> (o, lse)   the same with each head's keys cut into
+    fwd_split(q, k, v, nsplit=None) -> (o, lse)   the same with each head's keys cut into
                                                   nsplit ranges and merged (few heads)
     naive_fwd(q, k, v, scale=None)  -> (o, lse)   materialised S/P contrast path
     bwd(q, k, v, o, lse, dout)      -> (dq, dk, dv)  backward pass (recomputes P)
@@ -80,14 +80,22 @@ def split_workspace_bytes(B: int, H: int, N: int, d: int, nsplit: int) -> int:
     return int(_lib.load().fa_fwd_split_workspace_bytes(B, H, N, d, nsplit))
 
 
-def fwd_split(q, k, v, nsplit: int, scale: float | None = None, out=None, lse=None,
-              workspace=None, stream=None):
+def split_suggest(B: int, H: int, N: int, d: int, compute_units: int) -> int:
+    return int(_lib.load().fa_fwd_split_suggest(B, H, N, d, compute_units))
+
+
+def fwd_split(q, k, v, nsplit: int | None = None, scale: float | None = None, out=None,
+              lse=None, workspace=None, stream=None):
     """Key-split fused forward (16-bit inputs): returns (o, lse), equal to fwd()'s within
-    rounding.  workspace: optional uint8 device tensor of at least
+    rounding.  nsplit: key ranges per head (default: fa_fwd_split_suggest for the
+    device's compute units).  workspace: optional uint8 device tensor of at least
     split_workspace_bytes(B, H, N, d, nsplit) bytes, 256-byte aligned (allocated when
     omitted)."""
     _check_inputs(q, k, v)
     B, H, N, d = q.shape
+    if nsplit is None:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        nsplit = split_suggest(B, H, N, d, cus)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out, lse = _outputs(q, out, lse)
     nbytes = split_workspace_bytes(B, H, N, d, nsplit)

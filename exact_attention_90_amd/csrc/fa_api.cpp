@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -103,6 +104,17 @@ SplitLayout split_layout(int B, int H, int N, int d, int nsplit) {
   return L;
 }
 }  // namespace
+
+int fa_fwd_split_suggest(int B, int H, int N, int d, int compute_units) {
+  if (B <= 0 || H <= 0 || N <= 0 || compute_units <= 0) return 1;
+  if (d != 64 && d != 128 && d != 256) return 1;
+  const int64_t rows_per_wg = d == 128 ? 256 : 128;  // query rows per fused workgroup
+  const int64_t wgs = int64_t(B) * H * ((N + rows_per_wg - 1) / rows_per_wg);
+  if (wgs >= compute_units) return 1;
+  const int64_t want = (compute_units + wgs - 1) / wgs;
+  const int64_t cap = std::max<int64_t>(1, ((N + 63) / 64) / 8);  // >= 8 key tiles per range
+  return int(std::min<int64_t>({want, cap, int64_t(FA_MAX_SPLIT)}));
+}
 
 size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int nsplit) {
   if (B < 0 || H < 0 || N < 0 || nsplit < 1 || nsplit > FA_MAX_SPLIT) return 0;

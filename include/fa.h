@@ -129,6 +129,16 @@ int fa_fwd_split(const void *q, const void *k, const void *v, float *o, float *l
                  void *stream);
 
 /*
+ * fa_fwd_split_suggest - the number of key ranges for fa_fwd_split on a device with
+ * `compute_units` compute units (256 on MI355X): 1 when fa_fwd's grid (one workgroup
+ * per head and 256 query rows at d = 128, 128 rows otherwise) already has at least one
+ * workgroup per compute unit, else enough ranges to reach that, capped so that every
+ * range keeps at least 8 key tiles (512 keys) and at FA_MAX_SPLIT.  Pure arithmetic on
+ * its arguments; returns 1 for empty or invalid sizes.
+ */
+int fa_fwd_split_suggest(int B, int H, int N, int d, int compute_units);
+
+/*
  * Workspace bytes fa_fwd_split needs for these sizes: nsplit * B * H * N * (d + 1)
  * float32 values, each of the two parts rounded up to 256 bytes.  0 for negative
  * sizes, d not in {64, 128, 256} or nsplit outside 1 .. FA_MAX_SPLIT; SIZE_MAX if

@@ -163,6 +163,23 @@ def test_split_workspace_bytes(lib):
     assert lib.fa_fwd_split_workspace_bytes(0, 1, 3, 64, 2) == 0
 
 
+def test_split_suggest(lib):
+    s = lib.fa_fwd_split_suggest
+    # the measured cases on 256 compute units: one head of 16384 rows has 64 Q tiles,
+    # four ranges fill the device; four heads already have 256 Q tiles
+    assert s(1, 1, 16384, 128, 256) == 4
+    assert s(1, 4, 16384, 128, 256) == 1
+    assert s(1, 16, 16384, 128, 256) == 1
+    assert s(1, 8, 8192, 128, 256) == 1
+    assert s(1, 1, 16384, 64, 256) == 2          # 128-row tiles at d = 64
+    assert s(1, 1, 2048, 128, 256) == 4          # capped: 32 key tiles, 8 per range
+    assert s(1, 1, 100, 128, 256) == 1           # two key tiles: no split
+    assert s(1, 1, 2**20, 128, 100000) == 25     # ceil(100000 / 4096 Q tiles)
+    assert s(1, 1, 2**20, 128, 2**30) == 64      # FA_MAX_SPLIT
+    assert s(0, 1, 100, 128, 256) == 1 and s(1, 1, 100, 96, 256) == 1
+    assert s(1, 1, 100, 128, 0) == 1
+
+
 def _gpu_present():
     return os.path.exists("/dev/kfd")
 

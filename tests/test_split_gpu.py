@@ -104,3 +104,20 @@ def test_split_long_sequence_few_heads_sampled():
     say(f"c5 split: {m}")
     assert_parity(m, w.dtype, where="c5 split")
     assert bool(np.isfinite(o.cpu().numpy()).all())
+
+
+def test_split_default_count_from_the_device():
+    import exact_attention_90_amd as fa
+    import torch
+
+    B, H, N, d, dtype = 1, 1, 2048, 128, "bf16"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    say(f"default split count: {fa.split_suggest(B, H, N, d, cus)} of {cus} compute units")
+    x = make_qkv(B, H, N, d, dtype, seed=8)
+    scale32 = float(np.float32(1.0 / math.sqrt(d)))
+    xd = to_device(x, dtype)
+    o, lse = fa.fwd_split(xd["q"], xd["k"], xd["v"], scale=scale32)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], dtype, scale32)
+    assert_parity(metrics(o.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref), dtype,
+                  where="default split")
