@@ -86,7 +86,7 @@ def split_suggest(B: int, H: int, N: int, d: int, compute_units: int) -> int:
 
 def fwd_split(q, k, v, nsplit: int | None = None, scale: float | None = None, out=None,
               lse=None, workspace=None, stream=None):
-    """Key-split fused forward (16-bit inputs): returns (o, lse), equal to fwd()'s within
+    """Key-split fused forward: returns (o, lse), equal to fwd()'s within
     rounding.  nsplit: key ranges per head (default: fa_fwd_split_suggest for the
     device's compute units).  workspace: optional uint8 device tensor of at least
     split_workspace_bytes(B, H, N, d, nsplit) bytes, 256-byte aligned (allocated when

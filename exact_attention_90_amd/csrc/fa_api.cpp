@@ -131,7 +131,6 @@ int fa_fwd_split(const void *q, const void *k, const void *v, float *o, float *l
   bool empty = false;
   int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
   if (rc != FA_OK) return rc;
-  if (dtype == FA_F32) return FA_ERR_DTYPE;
   if (nsplit < 1 || nsplit > FA_MAX_SPLIT) return FA_ERR_SHAPE;
   if (empty) return FA_OK;
   if (!workspace || !aligned(workspace, 256)) return FA_ERR_WORKSPACE;

@@ -481,7 +481,8 @@ struct Cfg32 {
 template <int D>
 __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
-    float *__restrict__ O, float *__restrict__ LSE, int N, int nqt, int G, float c) {
+    float *__restrict__ O, float *__restrict__ LSE, int N, int nqt, int G, float c, int nsplit,
+    int kps) {
   using C = Cfg32<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *const Ks = smem;
@@ -489,10 +490,14 @@ __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
+  // work decomposition and key ranges as in fa_fwd16_kernel (nsplit = 1: whole head)
   const int L = xcd_remap(blockIdx.x, G);
-  const int bh = L / nqt, q0 = (L % nqt) * C::BM;
+  const int qt = L % nqt, kg = (L / nqt) % nsplit, bh = L / nqt / nsplit;
+  const int q0 = qt * C::BM;
   const int64_t hoff = int64_t(bh) * N * D;
-  const float *Qh = Q + hoff, *Kh = K + hoff, *Vh = V + hoff;
+  const int64_t bhn = int64_t(G / (nqt * nsplit)) * N;
+  const int kbeg = kg * kps, NK = min(N - kbeg, kps);
+  const float *Qh = Q + hoff, *Kh = K + hoff + int64_t(kbeg) * D, *Vh = V + hoff + int64_t(kbeg) * D;
 
 #pragma unroll
   for (int i = 0; i < C::QCPT; ++i) {
@@ -520,7 +525,7 @@ __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
       const int cid = i * 256 + tid, r = cid / C::CPR, ch = cid % C::CPR;
       const int key = kt * C::BN + r;
       kreg[i] = vreg[i] = u32x4{0u, 0u, 0u, 0u};
-      if (key < N) {
+      if (key < NK) {
         kreg[i] = *reinterpret_cast<const u32x4 *>(Kh + int64_t(key) * D + ch * 4);
         vreg[i] = *reinterpret_cast<const u32x4 *>(Vh + int64_t(key) * D + ch * 4);
       }
@@ -544,7 +549,7 @@ __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
   // the next tile's loads are issued before the current tile's compute; at d = 256 the
   // registers that would hold them in flight are not there, so they follow it
   constexpr bool PREFETCH = D <= 128;
-  const int nkt = (N + C::BN - 1) / C::BN;
+  const int nkt = (NK + C::BN - 1) / C::BN;
   fetch(0);
   stage(0);
   __syncthreads();
@@ -577,7 +582,7 @@ __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
       }
     }
 
-    const int nvalid = N - kt * C::BN;
+    const int nvalid = NK - kt * C::BN;
     if (nvalid < C::BN)
       softmax_tile<C::SB, C::OB, true>(s, o, mc, l, c, nvalid, h);
     else
@@ -609,7 +614,8 @@ __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
   }
 
   const int row = q0 + 32 * w + l32;
-  store_rows<C::OB>(o, mc, l, l, O + hoff + int64_t(row) * D, LSE + int64_t(bh) * N + row, h,
+  store_rows<C::OB>(o, mc, l, l, O + kg * bhn * D + hoff + int64_t(row) * D,
+                    LSE + kg * bhn + int64_t(bh) * N + row, h,
                     row < N);
 }
 
@@ -655,19 +661,27 @@ static hipError_t run16_any(const Problem &p, float *o, float *lse, int nsplit, 
 }
 
 template <int D>
-static hipError_t run32(const Problem &p, hipStream_t stream) {
+static hipError_t run32(const Problem &p, float *o, float *lse, int nsplit, int kps,
+                        hipStream_t stream) {
   using C = Cfg32<D>;
   auto kern = fa_fwd32_kernel<D>;
   // raise the dynamic-LDS cap once; a refusal surfaces as a launch error below
   static const hipError_t attr = allow_lds(kern, C::LDS);
   (void)attr;
   const int nqt = (p.N + C::BM - 1) / C::BM;
-  const int G = nqt * p.B * p.H;
+  const int G = nqt * p.B * p.H * nsplit;
   const float c = p.scale * kLog2e;
   hipLaunchKernelGGL(kern, dim3(G), dim3(256), C::LDS, stream,
                      static_cast<const float *>(p.q), static_cast<const float *>(p.k),
-                     static_cast<const float *>(p.v), p.o, p.lse, p.N, nqt, G, c);
+                     static_cast<const float *>(p.v), o, lse, p.N, nqt, G, c, nsplit, kps);
   return hipGetLastError();
+}
+
+static hipError_t run32_any(const Problem &p, float *o, float *lse, int nsplit, int kps,
+                            hipStream_t stream) {
+  return p.d == 256 ? run32<256>(p, o, lse, nsplit, kps, stream)
+         : p.d == 128 ? run32<128>(p, o, lse, nsplit, kps, stream)
+                      : run32<64>(p, o, lse, nsplit, kps, stream);
 }
 
 hipError_t launch_fused(const Problem &p, hipStream_t stream) {
@@ -677,9 +691,7 @@ hipError_t launch_fused(const Problem &p, hipStream_t stream) {
     case kBF16:
       return run16_any<true>(p, p.o, p.lse, 1, p.N, stream);
     default:
-      return p.d == 256 ? run32<256>(p, stream)
-             : p.d == 128 ? run32<128>(p, stream)
-                          : run32<64>(p, stream);
+      return run32_any(p, p.o, p.lse, 1, p.N, stream);
   }
 }
 
@@ -733,8 +745,9 @@ static hipError_t run_merge(const Problem &p, const float *opart, const float *l
 
 hipError_t launch_fused_split(const Problem &p, float *opart, float *lpart, int nsplit,
                               int kps, hipStream_t stream) {
-  hipError_t e = p.dtype == kBF16 ? run16_any<true>(p, opart, lpart, nsplit, kps, stream)
-                                  : run16_any<false>(p, opart, lpart, nsplit, kps, stream);
+  hipError_t e = p.dtype == kBF16  ? run16_any<true>(p, opart, lpart, nsplit, kps, stream)
+                 : p.dtype == kF16 ? run16_any<false>(p, opart, lpart, nsplit, kps, stream)
+                                   : run32_any(p, opart, lpart, nsplit, kps, stream);
   if (e != hipSuccess) return e;
   return p.d == 256 ? run_merge<256>(p, opart, lpart, nsplit, stream)
          : p.d == 128 ? run_merge<128>(p, opart, lpart, nsplit, stream)

@@ -41,7 +41,7 @@ struct BwdProblem {
 };
 
 hipError_t launch_fused(const Problem &p, hipStream_t stream);
-// 16-bit inputs: nsplit key ranges of kps keys into the partial buffers (opart: nsplit
+// nsplit key ranges of kps keys into the partial buffers (opart: nsplit
 // slots of B H N d floats, lpart: nsplit slots of B H N floats), then merged into p.o, p.lse
 hipError_t launch_fused_split(const Problem &p, float *opart, float *lpart, int nsplit,
                               int kps, hipStream_t stream);

@@ -111,7 +111,7 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
  * The same rule combines the partial results of a sequence split across GPUs.
  *
  *   q, k, v, o, lse, B, H, N, d, scale, stream   as for fa_fwd.
- *   dtype      FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_DTYPE).
+ *   dtype      FA_F32, FA_F16 or FA_BF16.
  *   nsplit     1 .. FA_MAX_SPLIT (else FA_ERR_SHAPE).  nsplit = 1 gives results
  *              bitwise equal to fa_fwd's.
  *   workspace  caller-owned device memory of fa_fwd_split_workspace_bytes(B, H, N,

@@ -139,7 +139,6 @@ def split_call(lib, ws=0x8000, nsplit=4, dtype=1, d=64, N=128, B=1, H=1, q=A):
 
 
 def test_split_rejects_bad_arguments(lib):
-    assert split_call(lib, dtype=0) == 4        # fp32 inputs: no key-split path
     assert split_call(lib, dtype=5) == 4
     assert split_call(lib, d=96) == 3
     assert split_call(lib, nsplit=0) == 2

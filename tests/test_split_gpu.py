@@ -4,7 +4,7 @@ Each head's keys are cut into ranges of whole 64-key tiles; the fused kernel com
 every range's (O_g, LSE_g) and a merge kernel combines them with the block-merge rule
 (Triton tutorial section 2.3).  The result is the full attention, so it is held to the
 same bar as fa_fwd: max |O - O_ref| <= 1e-2 and cosine >= 0.999 for 16-bit inputs,
-LSE within 1e-4 relative.
+<= 1e-5 for fp32 inputs, LSE within 1e-4 relative.
 """
 import math
 
@@ -47,6 +47,9 @@ def split_case(B, H, N, d, dtype, nsplit, seed, mult=1.0):
     (1, 1, 64, 128, "f16", 2),       # one key tile: one range runs
     (1, 3, 1, 64, "bf16", 4),        # one key
     (1, 1, 4096, 64, "f16", 64),     # the largest split, one tile per range
+    (1, 2, 300, 128, "f32", 3),      # fp32 inputs (fp32 matrix cores)
+    (1, 1, 200, 256, "f32", 2),      # fp32 at d = 256 (32-key tiles)
+    (2, 1, 129, 64, "f32", 4),
 ])
 def test_split_small_full(B, H, N, d, dtype, nsplit):
     m = split_case(B, H, N, d, dtype, nsplit, seed=N + d + nsplit)
