@@ -201,7 +201,7 @@ def main() -> int:
                     help="measure an ad-hoc shape instead of a named workload (N(0,1) inputs)")
     ap.add_argument("--path", default="fused", choices=["fused", "naive"])
     ap.add_argument("--split", type=int, default=0, metavar="S",
-                    help="fused path through fa_fwd_split with S key ranges per head "
+                    help="fa_fwd_split (or, with --pass bwd, fa_bwd_split) with S ranges per head "
                          "(for few heads and long sequences); 0 = fa_fwd")
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="fwd: the forward pass (the headline); bwd: the backward pass "
@@ -254,9 +254,6 @@ def main() -> int:
     o = torch.empty((w.B, w.H, w.N, w.d), dtype=torch.float32, device=dev)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     if args.which == "bwd":
-        if args.split:
-            print("bench.py: --split applies to the forward pass only", file=sys.stderr)
-            return 2
         return bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev)
     ws = None
     if args.split:
@@ -397,12 +394,19 @@ def bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev):
         g_np = g_np * 0
     g = torch.from_numpy(g_np).to(dev)
     fa.fwd(q, k, v, scale32, out=o, lse=lse)
-    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8,
-                     device=dev)
+    if args.split and w.dtype == "f32":
+        print("bench.py: --split with --pass bwd runs on 16-bit inputs", file=sys.stderr)
+        return 2
+    nbytes = (fa.bwd_split_workspace_bytes(w.B, w.H, w.N, w.d, q.dtype, args.split) if args.split
+              else fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d, q.dtype))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
 
     def step():
-        fa.bwd(q, k, v, o, lse, g, scale32, workspace=ws, grads=grads)
+        if args.split:
+            fa.bwd_split(q, k, v, o, lse, g, args.split, scale32, workspace=ws, grads=grads)
+        else:
+            fa.bwd(q, k, v, o, lse, g, scale32, workspace=ws, grads=grads)
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
@@ -422,7 +426,8 @@ def bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev):
     peak = PEAK_TFLOPS[w.dtype]
     rec = committed_traffic(w.name, "bwd")
     line = {
-        "metric": f"bwd attention TFLOP/s (5 products, 10 B H N^2 d), {w.short()}"
+        "metric": f"bwd attention TFLOP/s (5 products, 10 B H N^2 d"
+        + (f", {args.split} ranges summed" if args.split else "") + f"), {w.short()}"
         + (" [all-zero inputs: power diagnostic]" if args.zero_inputs else ""),
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
@@ -431,7 +436,7 @@ def bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev):
         "config": {"workload": f"{w.name}: attention backward (dQ, dK, dV from O, LSE, dO), "
                                f"{w.short()}, scale 1/sqrt({w.d})",
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "path": "fused",
-                   "parallelism": "single GPU"},
+                   "ranges": args.split or 1, "parallelism": "single GPU"},
         "pct_of_peak": round(100.0 * value / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(flops / (avg * 1e-3) / 1e12, 3),
                      "peak": peak, "unit": "TFLOP/s",

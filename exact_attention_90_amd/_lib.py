@@ -24,6 +24,7 @@ STATUS = {
 }
 # every symbol include/fa.h declares
 EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_split_suggest", "fa_fwd_split_workspace_bytes", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes",
+           "fa_bwd_split", "fa_bwd_split_workspace_bytes", "fa_bwd_split_suggest",
            "fa_status_string", "fa_version", "fa_last_hip_error")
 
 _lib = None
@@ -62,6 +63,12 @@ def load():
     lib.fa_bwd.restype = I
     lib.fa_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_split.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, F, I, P]
+    lib.fa_bwd_split.restype = I
+    lib.fa_bwd_split_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.fa_bwd_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.fa_bwd_split_suggest.argtypes = [I, I, I, I, I]
+    lib.fa_bwd_split_suggest.restype = I
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []

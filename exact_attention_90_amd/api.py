@@ -8,6 +8,7 @@ in the library's HIP kernels.  The function names follow the C boundary:
                                                   nsplit ranges and merged (few heads)
     naive_fwd(q, k, v, scale=None)  -> (o, lse)   materialised S/P contrast path
     bwd(q, k, v, o, lse, dout)      -> (dq, dk, dv)  backward pass (recomputes P)
+    bwd_split(q, k, v, o, lse, dout, nsplit=None)  the same with ranges of rows (few heads)
 
 q, k, v: contiguous [B, H, N, d] device tensors of one dtype (float32, float16 or
 bfloat16), d in {64, 128, 256}.  o is float32 [B, H, N, d]; lse is float32 [B, H, N]
@@ -177,6 +178,50 @@ def bwd(q, k, v, o, lse, dout, scale: float | None = None, workspace=None, grads
                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                     workspace.data_ptr(), B, H, N, d, scale, _CODES[q.dtype], _stream(q, stream))
     _lib.check(rc, "fa_bwd")
+    return dq, dk, dv
+
+
+def bwd_split_workspace_bytes(B: int, H: int, N: int, d: int, dtype, nsplit: int) -> int:
+    code = _CODES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(_lib.load().fa_bwd_split_workspace_bytes(B, H, N, d, code, nsplit))
+
+
+def bwd_split_suggest(B: int, H: int, N: int, d: int, compute_units: int) -> int:
+    return int(_lib.load().fa_bwd_split_suggest(B, H, N, d, compute_units))
+
+
+def bwd_split(q, k, v, o, lse, dout, nsplit: int | None = None, scale: float | None = None,
+              workspace=None, grads=None, stream=None):
+    """Backward pass with the key-owned kernel's queries and the query-owned kernel's keys
+    cut into ranges whose partial gradients are added (16-bit inputs): returns (dq, dk, dv)
+    like bwd().  nsplit defaults to fa_bwd_split_suggest for the device."""
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for name, t, shape in (("o", o, q.shape), ("dout", dout, q.shape), ("lse", lse, q.shape[:3])):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.shape != shape
+                or not t.is_contiguous() or t.device != q.device):
+            raise ValueError(f"{name} must be a contiguous float32 {tuple(shape)} tensor on {q.device}")
+    if nsplit is None:
+        cus = torch.cuda.get_device_properties(q.device).multi_processor_count
+        nsplit = bwd_split_suggest(B, H, N, d, cus)
+    if grads is None:
+        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    dq, dk, dv = grads
+    for t in grads:
+        if t.dtype != torch.float32 or t.shape != q.shape or not t.is_contiguous():
+            raise ValueError("grads must be contiguous float32 tensors shaped like q")
+    nbytes = bwd_split_workspace_bytes(B, H, N, d, q.dtype, nsplit)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError("split backward workspace too small")
+    lib = _lib.load()
+    rc = lib.fa_bwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                          dv.data_ptr(), workspace.data_ptr(), int(nsplit), B, H, N, d, scale,
+                          _CODES[q.dtype], _stream(q, stream))
+    _lib.check(rc, "fa_bwd_split")
     return dq, dk, dv
 
 

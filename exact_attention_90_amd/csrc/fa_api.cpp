@@ -242,6 +242,86 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
   return hip_status(fa::launch_bwd(p, static_cast<hipStream_t>(stream)));
 }
 
+// Workspace of the split backward: fa_bwd's workspace, then 3 nsplit slots of partial
+// gradients (B H N d floats each), 256-byte aligned.
+namespace {
+unsigned __int128 bwd_split_parts_offset(int B, int H, int N, int d, int dtype) {
+  return bwd_layout(B, H, N, d, dtype).total;
+}
+unsigned __int128 bwd_split_total(int B, int H, int N, int d, int dtype, int nsplit) {
+  const unsigned __int128 slot = (unsigned __int128)(uint64_t)B * (uint64_t)H * (uint64_t)N *
+                                 (uint64_t)d * 4;
+  return bwd_split_parts_offset(B, H, N, d, dtype) + round256(slot * 3 * (uint64_t)nsplit);
+}
+}  // namespace
+
+size_t fa_bwd_split_workspace_bytes(int B, int H, int N, int d, int dtype, int nsplit) {
+  if (dtype == FA_F32 || !bwd_supported(d, dtype) || B < 0 || H < 0 || N < 0) return 0;
+  if (nsplit < 1 || nsplit > FA_MAX_SPLIT) return 0;
+  const unsigned __int128 t = bwd_split_total(B, H, N, d, dtype, nsplit);
+  if (t > (unsigned __int128)std::numeric_limits<size_t>::max())
+    return std::numeric_limits<size_t>::max();
+  return (size_t)t;
+}
+
+int fa_bwd_split_suggest(int B, int H, int N, int d, int compute_units) {
+  if (B <= 0 || H <= 0 || N <= 0 || compute_units <= 0) return 1;
+  if (d != 64 && d != 128 && d != 256) return 1;
+  // 128 keys or queries per workgroup; the query-owned kernel holds two workgroups per
+  // compute unit, so the grid is full at twice the unit count
+  const int64_t wgs = int64_t(B) * H * ((N + 127) / 128);
+  const int64_t full = 2 * int64_t(compute_units);
+  if (wgs >= full) return 1;
+  const int64_t want = (full + wgs - 1) / wgs;
+  const int64_t cap = std::max<int64_t>(1, ((N + 63) / 64) / 8);  // >= 8 tiles per range
+  return int(std::min<int64_t>({want, cap, int64_t(FA_MAX_SPLIT)}));
+}
+
+int fa_bwd_split(const void *q, const void *k, const void *v, const float *o, const float *lse,
+                 const float *dout, float *dq, float *dk, float *dv, void *workspace, int nsplit,
+                 int B, int H, int N, int d, float scale, int dtype, void *stream) {
+  bool empty = false;
+  int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
+  if (rc != FA_OK) return rc;
+  if (dtype == FA_F32) return FA_ERR_DTYPE;
+  if (!bwd_supported(d, dtype)) return FA_ERR_HEADDIM;
+  if (nsplit < 1 || nsplit > FA_MAX_SPLIT) return FA_ERR_SHAPE;
+  if (empty) return FA_OK;
+  if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return FA_ERR_ALIGN;
+  if (!workspace || !aligned(workspace, 256)) return FA_ERR_WORKSPACE;
+  const int tiles = (N + 63) / 64;
+  const int tps = (tiles + nsplit - 1) / nsplit;
+  const int used = (tiles + tps - 1) / tps;
+  if (int64_t(B) * H * ((int64_t(N) + 127) / 128) * used > fa::kMaxGrid) return FA_ERR_SHAPE;
+  rc = device_ready();
+  if (rc != FA_OK) return rc;
+  const BwdLayout L = bwd_layout(B, H, N, d, dtype);
+  char *ws = static_cast<char *>(workspace);
+  fa::BwdProblem p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.dout = dout;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.ws_do16 = ws + (size_t)L.do16;
+  p.ws_lse2 = reinterpret_cast<float *>(ws + (size_t)L.lse2);
+  p.ws_d = reinterpret_cast<float *>(ws + (size_t)L.d);
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.d = d;
+  p.scale = scale;
+  p.dtype = dtype;
+  float *parts = reinterpret_cast<float *>(ws + (size_t)bwd_split_parts_offset(B, H, N, d, dtype));
+  return hip_status(fa::launch_bwd_split(p, parts, used, tps, static_cast<hipStream_t>(stream)));
+}
+
 const char *fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

@@ -194,7 +194,7 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO16,
     const float *__restrict__ lse2, const float *__restrict__ Dv, float *__restrict__ dK,
-    float *__restrict__ dV, int N, int nkb, int G, float c, float scale) {
+    float *__restrict__ dV, int N, int nkb, int G, float c, float scale, int nsplit, int tps) {
   using C = CfgB<D, WAVES>;
   constexpr int KC = C::KC, OB = C::OB, CPT = C::CPT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -206,9 +206,14 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  // workgroup L: key block L % nkb, query range (L / nkb) % nsplit (query tiles
+  // [rg tps, min(nqt, (rg + 1) tps)), never empty), head L / (nkb nsplit).  Its dK and dV
+  // over that range go to slot rg of dK and dV (slots B H N d values apart); with
+  // nsplit = 1 the range is every query and the slot is the gradient itself.
   const int L = xcd_remap(blockIdx.x, G);
-  const int bh = L / nkb, k0 = (L % nkb) * C::BR;
+  const int rg = (L / nkb) % nsplit, bh = L / nkb / nsplit, k0 = (L % nkb) * C::BR;
   const int64_t hoff = int64_t(bh) * N * D;
+  const int64_t slot = int64_t(G / (nkb * nsplit)) * N * D * rg;
   const uint32_t head_bytes = uint32_t(N) * C::ROWB;
   const auto qrs = make_rsrc(Q + hoff, head_bytes);
   const auto grs = make_rsrc(dO16 + hoff, head_bytes);
@@ -260,7 +265,8 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
     if constexpr (WANT_DV) dv[e] = f32x16{};
   }
 
-  const int nqt = (N + C::BT - 1) / C::BT;
+  const int qt0 = rg * tps;                                       // first query tile
+  const int nqt = min((N + C::BT - 1) / C::BT - qt0, tps);         // tiles of the range
   // LDS addresses of the operand reads in the current stage, one per k-step (row reads)
   // and per output block (transposing reads); the dO tiles are an immediate offset from
   // them.  The stages are TILEB (statistics: STATB) apart, so one add per register moves
@@ -278,13 +284,13 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
   uint32_t stat_off = q_lds + 4 * C::TILEB + 16 * h;
   constexpr int GS = 2 * C::TILEB;   // dO tile stage - Q tile stage
   constexpr int DS = 2 * C::STATB;   // D stage - lse2 stage
-  load_tile(0, 0);
+  load_tile(0, qt0);
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   lds_barrier();
-  for (int qt = 0; qt < nqt; ++qt) {
+  for (int qt = 0; qt < nqt; ++qt) {  // qt counts the range's tiles
     const int st = qt & 1;
     // the other stage held tile qt - 1, released by the barrier that ended it
-    if (qt + 1 < nqt) load_tile(st ^ 1, qt + 1);
+    if (qt + 1 < nqt) load_tile(st ^ 1, qt0 + qt + 1);
     // held in registers across the loop rather than recomputed at each read
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) pin(a_off[kc]);
@@ -499,10 +505,10 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
   // store_rows_lds divides by the pair sum of its normaliser: 1/scale for dK, 1 for dV
   if constexpr (WANT_DK)
     store_rows_lds<D, 1, false>(dk, 0.f, 1.f, 0.5f / scale, region,
-                                dK + hoff + int64_t(row0) * D, nullptr, lane, N - row0);
+                                dK + slot + hoff + int64_t(row0) * D, nullptr, lane, N - row0);
   if constexpr (WANT_DV)
-    store_rows_lds<D, 1, false>(dv, 0.f, 1.f, 0.5f, region, dV + hoff + int64_t(row0) * D,
-                                nullptr, lane, N - row0);
+    store_rows_lds<D, 1, false>(dv, 0.f, 1.f, 0.5f, region,
+                                dV + slot + hoff + int64_t(row0) * D, nullptr, lane, N - row0);
 }
 
 // ------------------------------------------------------------------------------------
@@ -513,7 +519,7 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, const uint16_t *__restrict__ dO16,
     const float *__restrict__ lse2, const float *__restrict__ Dv, float *__restrict__ dQ, int N,
-    int nqb, int G, float c, float scale) {
+    int nqb, int G, float c, float scale, int nsplit, int tps) {
   using C = CfgB<D, WAVES>;
   constexpr int KC = C::KC, OB = C::OB, CPT = C::CPT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -523,9 +529,13 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  // workgroup L: query block L % nqb, key range (L / nqb) % nsplit (key tiles
+  // [rg tps, min(nkt, (rg + 1) tps))), head L / (nqb nsplit); its dQ over that range goes
+  // to slot rg of dQ, as in the dK/dV kernel
   const int L = xcd_remap(blockIdx.x, G);
-  const int bh = L / nqb, q0 = (L % nqb) * C::BR;
+  const int rg = (L / nqb) % nsplit, bh = L / nqb / nsplit, q0 = (L % nqb) * C::BR;
   const int64_t hoff = int64_t(bh) * N * D;
+  const int64_t slot = int64_t(G / (nqb * nsplit)) * N * D * rg;
   const uint32_t head_bytes = uint32_t(N) * C::ROWB;
   const auto qrs = make_rsrc(Q + hoff, head_bytes);
   const auto grs = make_rsrc(dO16 + hoff, head_bytes);
@@ -565,13 +575,14 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
 #pragma unroll
   for (int e = 0; e < OB; ++e) dq[e] = f32x16{};
 
-  const int nkt = (N + C::BT - 1) / C::BT;
-  load_tile(0, 0);
+  const int kt0 = rg * tps;                                       // first key tile
+  const int nkt = min((N + C::BT - 1) / C::BT - kt0, tps);         // tiles of the range
+  load_tile(0, kt0);
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   lds_barrier();
-  for (int kt = 0; kt < nkt; ++kt) {
+  for (int kt = 0; kt < nkt; ++kt) {  // kt counts the range's tiles
     const int st = kt & 1;
-    if (kt + 1 < nkt) load_tile(st ^ 1, kt + 1);
+    if (kt + 1 < nkt) load_tile(st ^ 1, kt0 + kt + 1);
     const int kb = st * C::TILEB;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // 32-key blocks of the tile
@@ -611,7 +622,7 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
   constexpr int WAVE_LDS = (C::LDS / WAVES) & ~15;
   const int row0 = q0 + 32 * w;
   store_rows_lds<D, 1, false>(dq, 0.f, 1.f, 0.5f / scale, smem + w * WAVE_LDS,
-                       dQ + hoff + int64_t(row0) * D, nullptr, lane, N - row0);
+                       dQ + slot + hoff + int64_t(row0) * D, nullptr, lane, N - row0);
 }
 
 // ------------------------------------------------------------------------------------
@@ -621,8 +632,11 @@ static hipError_t allow_lds_bwd(KernelT kernel, int bytes) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+// nsplit ranges of tps streamed tiles each; dq, dk, dv receive nsplit slots of B H N d
+// floats (with nsplit = 1 they are the gradients themselves)
 template <int D, bool BF16>
-static hipError_t run_bwd(const BwdProblem &p, hipStream_t stream) {
+static hipError_t run_bwd(const BwdProblem &p, float *dq, float *dk, float *dv, int nsplit,
+                          int tps, hipStream_t stream) {
   constexpr int WAVES = 4;
   using C = CfgB<D, WAVES>;
   const int64_t rows = int64_t(p.B) * p.H * p.N;
@@ -638,7 +652,7 @@ static hipError_t run_bwd(const BwdProblem &p, hipStream_t stream) {
   }
   const float c = p.scale * kLog2e;
   const int nb = (p.N + C::BR - 1) / C::BR;
-  const int G = nb * p.B * p.H;
+  const int G = nb * p.B * p.H * nsplit;
   // dK and dV: one launch, or (d = 256) one for dV and one for dK
   auto dkdv = [&](auto what) -> hipError_t {
     auto kern = fa_bwd_dkdv_kernel<D, BF16, WAVES, decltype(what)::value>;
@@ -646,8 +660,8 @@ static hipError_t run_bwd(const BwdProblem &p, hipStream_t stream) {
     (void)attr;
     hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
                        static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
-                       static_cast<const uint16_t *>(p.v), dO16, p.ws_lse2, p.ws_d, p.dk, p.dv,
-                       p.N, nb, G, c, p.scale);
+                       static_cast<const uint16_t *>(p.v), dO16, p.ws_lse2, p.ws_d, dk, dv,
+                       p.N, nb, G, c, p.scale, nsplit, tps);
     return hipGetLastError();
   };
   {
@@ -666,21 +680,68 @@ static hipError_t run_bwd(const BwdProblem &p, hipStream_t stream) {
     (void)attr;
     hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
                        static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
-                       static_cast<const uint16_t *>(p.v), dO16, p.ws_lse2, p.ws_d, p.dq, p.N,
-                       nb, G, c, p.scale);
+                       static_cast<const uint16_t *>(p.v), dO16, p.ws_lse2, p.ws_d, dq, p.N,
+                       nb, G, c, p.scale, nsplit, tps);
   }
   return hipGetLastError();
 }
 
+template <bool BF16>
+static hipError_t run_bwd_any(const BwdProblem &p, float *dq, float *dk, float *dv, int nsplit,
+                              int tps, hipStream_t stream) {
+  return p.d == 256   ? run_bwd<256, BF16>(p, dq, dk, dv, nsplit, tps, stream)
+         : p.d == 128 ? run_bwd<128, BF16>(p, dq, dk, dv, nsplit, tps, stream)
+                      : run_bwd<64, BF16>(p, dq, dk, dv, nsplit, tps, stream);
+}
+
 hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream) {
   if (p.dtype == kF32) return launch_bwd32(p, stream);
-  if (p.dtype == kBF16)
-    return p.d == 256   ? run_bwd<256, true>(p, stream)
-           : p.d == 128 ? run_bwd<128, true>(p, stream)
-                        : run_bwd<64, true>(p, stream);
-  return p.d == 256   ? run_bwd<256, false>(p, stream)
-         : p.d == 128 ? run_bwd<128, false>(p, stream)
-                      : run_bwd<64, false>(p, stream);
+  const int tiles = (p.N + 63) / 64;
+  return p.dtype == kBF16 ? run_bwd_any<true>(p, p.dq, p.dk, p.dv, 1, tiles, stream)
+                          : run_bwd_any<false>(p, p.dq, p.dk, p.dv, 1, tiles, stream);
+}
+
+// ------------------------------------------------------------------------------------
+// Split backward: the key-owned kernel's query tiles and the query-owned kernel's key
+// tiles are cut into nsplit ranges (every range non-empty), each range's dQ, dK and dV
+// go to their own slot of the partial buffers, and fa_sum_slots adds the slots in slot
+// order (so results are bitwise reproducible) into the gradients.  The gradients are
+// sums over keys (dQ) or queries (dK, dV) of per-pair terms, so the ranges add.
+// ------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void fa_sum_slots(const float *__restrict__ part,
+                                                    float *__restrict__ out, int64_t n4,
+                                                    int nsplit) {
+  // n4: float4 elements of one slot
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n4;
+       i += int64_t(gridDim.x) * 256) {
+    f32x4 acc = reinterpret_cast<const f32x4 *>(part)[i];
+    for (int g = 1; g < nsplit; ++g) {
+      const f32x4 v = reinterpret_cast<const f32x4 *>(part)[g * n4 + i];
+      acc = f32x4{acc[0] + v[0], acc[1] + v[1], acc[2] + v[2], acc[3] + v[3]};
+    }
+    reinterpret_cast<f32x4 *>(out)[i] = acc;
+  }
+}
+
+hipError_t launch_bwd_split(const BwdProblem &p, float *parts, int nsplit, int tps,
+                            hipStream_t stream) {
+  const int64_t slot = int64_t(p.B) * p.H * p.N * p.d;  // floats of one slot
+  float *pq = parts, *pk = parts + nsplit * slot, *pv = parts + 2 * nsplit * slot;
+  hipError_t e = p.dtype == kBF16 ? run_bwd_any<true>(p, pq, pk, pv, nsplit, tps, stream)
+                                  : run_bwd_any<false>(p, pq, pk, pv, nsplit, tps, stream);
+  if (e != hipSuccess) return e;
+  const int64_t n4 = slot / 4;
+  const int64_t blocks = (n4 + 255) / 256;
+  const int grid = int(blocks < 65536 ? blocks : 65536);
+  const float *src[3] = {pq, pk, pv};
+  float *dst[3] = {p.dq, p.dk, p.dv};
+  for (int x = 0; x < 3; ++x) {
+    hipLaunchKernelGGL(fa_sum_slots, dim3(grid), dim3(256), 0, stream, src[x], dst[x], n4,
+                       nsplit);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace fa

@@ -213,6 +213,41 @@ int fa_bwd(const void *q, const void *k, const void *v, const float *o, const fl
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
 
+/*
+ * fa_bwd_split - fa_bwd for few heads and long sequences.  dK and dV are sums over
+ * query rows, and dQ a sum over key rows, of per-pair terms (the chain rule through
+ * O = P V and the softmax, as in fa_bwd).  Here the key-owned kernel's query tiles and
+ * the query-owned kernel's key tiles (64 rows each) are cut into up to nsplit ranges of
+ * ceil(ceil(N/64) / nsplit) tiles; every range writes its partial dQ, dK and dV to its
+ * own slot of the workspace, and a last kernel adds the slots in range order into dq,
+ * dk and dv.  Results are bitwise identical from run to run; nsplit = 1 gives fa_bwd's.
+ *
+ *   all arguments but workspace and nsplit   as for fa_bwd.
+ *   dtype      FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_DTYPE).
+ *   nsplit     1 .. FA_MAX_SPLIT (else FA_ERR_SHAPE).
+ *   workspace  fa_bwd_split_workspace_bytes(B, H, N, d, dtype, nsplit) bytes of device
+ *              memory, 256-byte aligned: fa_bwd's workspace followed by 3 nsplit
+ *              float32 slots of [B, H, N, d].
+ *
+ * Returns FA_OK or an fa_status error code.
+ */
+int fa_bwd_split(const void *q, const void *k, const void *v, const float *o, const float *lse,
+                 const float *dout, float *dq, float *dk, float *dv, void *workspace, int nsplit,
+                 int B, int H, int N, int d, float scale, int dtype, void *stream);
+
+/* Workspace bytes of fa_bwd_split: fa_bwd_workspace_bytes(B, H, N, d, dtype) plus
+ * 3 * nsplit * B * H * N * d float32 values rounded up to 256 bytes.  0 for FA_F32, an
+ * unsupported d, negative sizes or nsplit outside 1 .. FA_MAX_SPLIT; SIZE_MAX if the
+ * size does not fit a size_t. */
+size_t fa_bwd_split_workspace_bytes(int B, int H, int N, int d, int dtype, int nsplit);
+
+/* fa_bwd_split_suggest - as fa_fwd_split_suggest, for the backward pass's grids (one
+ * workgroup per head and 128 keys or queries; the query-owned kernel holds two per
+ * compute unit): the number of ranges that gives the grids two workgroups per compute
+ * unit, each range keeping at least 8 tiles; 1 when the grid is already that large or
+ * the sizes are empty or invalid. */
+int fa_bwd_split_suggest(int B, int H, int N, int d, int compute_units);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char *fa_status_string(int status);
 

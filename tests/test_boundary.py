@@ -179,6 +179,31 @@ def test_split_suggest(lib):
     assert s(1, 1, 100, 128, 0) == 1
 
 
+def test_bwd_split_arguments_and_sizes(lib):
+    def call(dtype=1, d=64, ws=0x8000, nsplit=2, N=128, dout=0x9000):
+        return lib.fa_bwd_split(A, B_, C_, O_, L_, dout, 0xa000, 0xb000, 0xc000, ws, nsplit,
+                                1, 1, N, d, 0.125, dtype, None)
+    assert call(dtype=0) == 4          # fp32 inputs: no split backward
+    assert call(d=96) == 3
+    assert call(nsplit=0) == 2 and call(nsplit=65) == 2
+    assert call(ws=0) == 7 and call(ws=0x8010) == 7
+    assert call(dout=0) == 1
+    assert call(N=0, ws=0, dout=0) == 0
+    # fa_bwd's workspace, then 3 nsplit slots of B H N d floats rounded up to 256 bytes
+    base = lib.fa_bwd_workspace_bytes(1, 2, 100, 64, 2)
+    assert lib.fa_bwd_split_workspace_bytes(1, 2, 100, 64, 2, 4) == base + 3 * 4 * 2 * 100 * 64 * 4
+    assert lib.fa_bwd_split_workspace_bytes(1, 1, 3, 64, 1, 1) == (
+        lib.fa_bwd_workspace_bytes(1, 1, 3, 64, 1) + 2304)
+    assert lib.fa_bwd_split_workspace_bytes(1, 1, 3, 64, 0, 2) == 0
+    assert lib.fa_bwd_split_workspace_bytes(1, 1, 3, 64, 1, 0) == 0
+    s = lib.fa_bwd_split_suggest
+    assert s(1, 1, 16384, 128, 256) == 4     # 128 workgroups of 128 rows (4: measured best)
+    assert s(1, 4, 16384, 128, 256) == 1     # 512 workgroups: two per compute unit
+    assert s(1, 2, 8192, 64, 256) == 4       # measured best at d = 64
+    assert s(1, 1, 4096, 64, 256) == 8       # 32 workgroups; capped at 64 tiles / 8
+    assert s(1, 1, 100, 64, 256) == 1
+
+
 def _gpu_present():
     return os.path.exists("/dev/kfd")
 
