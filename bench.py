@@ -394,9 +394,6 @@ def bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev):
         g_np = g_np * 0
     g = torch.from_numpy(g_np).to(dev)
     fa.fwd(q, k, v, scale32, out=o, lse=lse)
-    if args.split and w.dtype == "f32":
-        print("bench.py: --split with --pass bwd runs on 16-bit inputs", file=sys.stderr)
-        return 2
     nbytes = (fa.bwd_split_workspace_bytes(w.B, w.H, w.N, w.d, q.dtype, args.split) if args.split
               else fa.bwd_workspace_bytes(w.B, w.H, w.N, w.d, q.dtype))
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)

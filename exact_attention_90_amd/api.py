@@ -193,7 +193,7 @@ def bwd_split_suggest(B: int, H: int, N: int, d: int, compute_units: int) -> int
 def bwd_split(q, k, v, o, lse, dout, nsplit: int | None = None, scale: float | None = None,
               workspace=None, grads=None, stream=None):
     """Backward pass with the key-owned kernel's queries and the query-owned kernel's keys
-    cut into ranges whose partial gradients are added (16-bit inputs): returns (dq, dk, dv)
+    cut into ranges whose partial gradients are added: returns (dq, dk, dv)
     like bwd().  nsplit defaults to fa_bwd_split_suggest for the device."""
     _check_inputs(q, k, v)
     B, H, N, d = q.shape

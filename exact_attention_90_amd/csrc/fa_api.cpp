@@ -256,7 +256,7 @@ unsigned __int128 bwd_split_total(int B, int H, int N, int d, int dtype, int nsp
 }  // namespace
 
 size_t fa_bwd_split_workspace_bytes(int B, int H, int N, int d, int dtype, int nsplit) {
-  if (dtype == FA_F32 || !bwd_supported(d, dtype) || B < 0 || H < 0 || N < 0) return 0;
+  if (!bwd_supported(d, dtype) || B < 0 || H < 0 || N < 0) return 0;
   if (nsplit < 1 || nsplit > FA_MAX_SPLIT) return 0;
   const unsigned __int128 t = bwd_split_total(B, H, N, d, dtype, nsplit);
   if (t > (unsigned __int128)std::numeric_limits<size_t>::max())
@@ -283,8 +283,7 @@ int fa_bwd_split(const void *q, const void *k, const void *v, const float *o, co
   bool empty = false;
   int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
   if (rc != FA_OK) return rc;
-  if (dtype == FA_F32) return FA_ERR_DTYPE;
-  if (!bwd_supported(d, dtype)) return FA_ERR_HEADDIM;
+  if (!bwd_supported(d, dtype)) return FA_ERR_HEADDIM;  // fp32 inputs at d = 256
   if (nsplit < 1 || nsplit > FA_MAX_SPLIT) return FA_ERR_SHAPE;
   if (empty) return FA_OK;
   if (!dout || !dq || !dk || !dv) return FA_ERR_NULL;

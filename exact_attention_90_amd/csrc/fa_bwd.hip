@@ -727,8 +727,9 @@ hipError_t launch_bwd_split(const BwdProblem &p, float *parts, int nsplit, int t
                             hipStream_t stream) {
   const int64_t slot = int64_t(p.B) * p.H * p.N * p.d;  // floats of one slot
   float *pq = parts, *pk = parts + nsplit * slot, *pv = parts + 2 * nsplit * slot;
-  hipError_t e = p.dtype == kBF16 ? run_bwd_any<true>(p, pq, pk, pv, nsplit, tps, stream)
-                                  : run_bwd_any<false>(p, pq, pk, pv, nsplit, tps, stream);
+  hipError_t e = p.dtype == kBF16  ? run_bwd_any<true>(p, pq, pk, pv, nsplit, tps, stream)
+                 : p.dtype == kF16 ? run_bwd_any<false>(p, pq, pk, pv, nsplit, tps, stream)
+                                   : launch_bwd32_ranges(p, pq, pk, pv, nsplit, tps, stream);
   if (e != hipSuccess) return e;
   const int64_t n4 = slot / 4;
   const int64_t blocks = (n4 + 255) / 256;

@@ -87,7 +87,8 @@ template <int D>
 __global__ __launch_bounds__(256, 1) void fa_bwd32_dkdv_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     const float *__restrict__ dO, const float *__restrict__ lse2, const float *__restrict__ Dv,
-    float *__restrict__ dK, float *__restrict__ dV, int N, int nkb, int G, float c, float scale) {
+    float *__restrict__ dK, float *__restrict__ dV, int N, int nkb, int G, float c, float scale,
+    int nsplit, int tps) {
   using C = CfgB32<D>;
   constexpr int KC = C::KC, OB = C::OB, CPT = C::CPT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -99,9 +100,12 @@ __global__ __launch_bounds__(256, 1) void fa_bwd32_dkdv_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  // key block L % nkb, query-tile range (L / nkb) % nsplit, head L / (nkb nsplit); the
+  // range's dK and dV go to its slot (as in the 16-bit kernel)
   const int L = xcd_remap(blockIdx.x, G);
-  const int bh = L / nkb, k0 = (L % nkb) * C::BR;
+  const int rg = (L / nkb) % nsplit, bh = L / nkb / nsplit, k0 = (L % nkb) * C::BR;
   const int64_t hoff = int64_t(bh) * N * D;
+  const int64_t slot = int64_t(G / (nkb * nsplit)) * N * D * rg;
   const uint32_t head_bytes = uint32_t(N) * C::ROWB;
   const auto qrs = make_rsrc(Q + hoff, head_bytes);
   const auto grs = make_rsrc(dO + hoff, head_bytes);
@@ -137,13 +141,14 @@ __global__ __launch_bounds__(256, 1) void fa_bwd32_dkdv_kernel(
 #pragma unroll
   for (int e = 0; e < OB; ++e) dk[e] = dv[e] = f32x16{};
 
-  const int nqt = (N + C::BT - 1) / C::BT;
-  load_tile(0, 0);
+  const int qt0 = rg * tps;                                // first query tile
+  const int nqt = min((N + C::BT - 1) / C::BT - qt0, tps);  // tiles of the range
+  load_tile(0, qt0);
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   lds_barrier();
-  for (int qt = 0; qt < nqt; ++qt) {
+  for (int qt = 0; qt < nqt; ++qt) {  // qt counts the range's tiles
     const int st = qt & 1;
-    if (qt + 1 < nqt) load_tile(st ^ 1, qt + 1);
+    if (qt + 1 < nqt) load_tile(st ^ 1, qt0 + qt + 1);
     const char *qs = Qs + st * C::TILEB, *gs = Gs + st * C::TILEB;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -195,9 +200,9 @@ __global__ __launch_bounds__(256, 1) void fa_bwd32_dkdv_kernel(
   constexpr int WAVE_LDS = (C::LDS / 4) & ~15;
   const int row0 = k0 + 32 * w;
   char *region = smem + w * WAVE_LDS;
-  store_rows_lds<D, 1, false>(dk, 0.f, 1.f, 0.5f / scale, region, dK + hoff + int64_t(row0) * D,
+  store_rows_lds<D, 1, false>(dk, 0.f, 1.f, 0.5f / scale, region, dK + slot + hoff + int64_t(row0) * D,
                               nullptr, lane, N - row0);
-  store_rows_lds<D, 1, false>(dv, 0.f, 1.f, 0.5f, region, dV + hoff + int64_t(row0) * D, nullptr,
+  store_rows_lds<D, 1, false>(dv, 0.f, 1.f, 0.5f, region, dV + slot + hoff + int64_t(row0) * D, nullptr,
                               lane, N - row0);
 }
 
@@ -208,7 +213,7 @@ template <int D>
 __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void fa_bwd32_dq_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     const float *__restrict__ dO, const float *__restrict__ lse2, const float *__restrict__ Dv,
-    float *__restrict__ dQ, int N, int nqb, int G, float c, float scale) {
+    float *__restrict__ dQ, int N, int nqb, int G, float c, float scale, int nsplit, int tps) {
   using C = CfgB32<D>;
   constexpr int KC = C::KC, OB = C::OB, CPT = C::CPT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -218,9 +223,11 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void fa_bwd32_dq_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  // query block L % nqb, key-tile range (L / nqb) % nsplit, head L / (nqb nsplit)
   const int L = xcd_remap(blockIdx.x, G);
-  const int bh = L / nqb, q0 = (L % nqb) * C::BR;
+  const int rg = (L / nqb) % nsplit, bh = L / nqb / nsplit, q0 = (L % nqb) * C::BR;
   const int64_t hoff = int64_t(bh) * N * D;
+  const int64_t slot = int64_t(G / (nqb * nsplit)) * N * D * rg;
   const uint32_t head_bytes = uint32_t(N) * C::ROWB;
   const auto qrs = make_rsrc(Q + hoff, head_bytes);
   const auto grs = make_rsrc(dO + hoff, head_bytes);
@@ -254,13 +261,14 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void fa_bwd32_dq_kernel(
 #pragma unroll
   for (int e = 0; e < OB; ++e) dq[e] = f32x16{};
 
-  const int nkt = (N + C::BT - 1) / C::BT;
-  load_tile(0, 0);
+  const int kt0 = rg * tps;                                // first key tile
+  const int nkt = min((N + C::BT - 1) / C::BT - kt0, tps);  // tiles of the range
+  load_tile(0, kt0);
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
   lds_barrier();
-  for (int kt = 0; kt < nkt; ++kt) {
+  for (int kt = 0; kt < nkt; ++kt) {  // kt counts the range's tiles
     const int st = kt & 1;
-    if (kt + 1 < nkt) load_tile(st ^ 1, kt + 1);
+    if (kt + 1 < nkt) load_tile(st ^ 1, kt0 + kt + 1);
     const char *ks = Ks + st * C::TILEB, *vs = Vs + st * C::TILEB;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -297,12 +305,13 @@ __global__ __launch_bounds__(256, D >= 128 ? 1 : 2) void fa_bwd32_dq_kernel(
   constexpr int WAVE_LDS = (C::LDS / 4) & ~15;
   const int row0 = q0 + 32 * w;
   store_rows_lds<D, 1, false>(dq, 0.f, 1.f, 0.5f / scale, smem + w * WAVE_LDS,
-                              dQ + hoff + int64_t(row0) * D, nullptr, lane, N - row0);
+                              dQ + slot + hoff + int64_t(row0) * D, nullptr, lane, N - row0);
 }
 
 // ------------------------------------------------------------------------------------
 template <int D>
-static hipError_t run_bwd32(const BwdProblem &p, hipStream_t stream) {
+static hipError_t run_bwd32(const BwdProblem &p, float *dq, float *dk, float *dv, int nsplit,
+                            int tps, hipStream_t stream) {
   using C = CfgB32<D>;
   const int64_t rows = int64_t(p.B) * p.H * p.N;
   {
@@ -315,7 +324,7 @@ static hipError_t run_bwd32(const BwdProblem &p, hipStream_t stream) {
   }
   const float c = p.scale * kLog2e;
   const int nb = (p.N + C::BR - 1) / C::BR;
-  const int G = nb * p.B * p.H;
+  const int G = nb * p.B * p.H * nsplit;
   const float *q = static_cast<const float *>(p.q), *k = static_cast<const float *>(p.k),
               *v = static_cast<const float *>(p.v);
   {
@@ -324,7 +333,7 @@ static hipError_t run_bwd32(const BwdProblem &p, hipStream_t stream) {
         reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     (void)attr;
     hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream, q, k, v, p.dout, p.ws_lse2,
-                       p.ws_d, p.dk, p.dv, p.N, nb, G, c, p.scale);
+                       p.ws_d, dk, dv, p.N, nb, G, c, p.scale, nsplit, tps);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -334,13 +343,19 @@ static hipError_t run_bwd32(const BwdProblem &p, hipStream_t stream) {
         reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
     (void)attr;
     hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream, q, k, v, p.dout, p.ws_lse2,
-                       p.ws_d, p.dq, p.N, nb, G, c, p.scale);
+                       p.ws_d, dq, p.N, nb, G, c, p.scale, nsplit, tps);
   }
   return hipGetLastError();
 }
 
+hipError_t launch_bwd32_ranges(const BwdProblem &p, float *dq, float *dk, float *dv, int nsplit,
+                               int tps, hipStream_t stream) {
+  return p.d == 128 ? run_bwd32<128>(p, dq, dk, dv, nsplit, tps, stream)
+                    : run_bwd32<64>(p, dq, dk, dv, nsplit, tps, stream);
+}
+
 hipError_t launch_bwd32(const BwdProblem &p, hipStream_t stream) {
-  return p.d == 128 ? run_bwd32<128>(p, stream) : run_bwd32<64>(p, stream);
+  return launch_bwd32_ranges(p, p.dq, p.dk, p.dv, 1, (p.N + 63) / 64, stream);
 }
 
 }  // namespace fa

@@ -46,11 +46,14 @@ hipError_t launch_fused(const Problem &p, hipStream_t stream);
 hipError_t launch_fused_split(const Problem &p, float *opart, float *lpart, int nsplit,
                               int kps, hipStream_t stream);
 hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream);    // every dtype
-// 16-bit inputs: nsplit ranges of tps tiles (64 rows) each; parts holds 3 nsplit slots of
+// nsplit ranges of tps tiles (64 rows) each; parts holds 3 nsplit slots of
 // B H N d floats (dQ slots, then dK, then dV), summed into p.dq, p.dk, p.dv
 hipError_t launch_bwd_split(const BwdProblem &p, float *parts, int nsplit, int tps,
                             hipStream_t stream);
 hipError_t launch_bwd32(const BwdProblem &p, hipStream_t stream);  // fp32 inputs
+// fp32 inputs, nsplit ranges of tps 64-row tiles into dq, dk, dv (nsplit slots each)
+hipError_t launch_bwd32_ranges(const BwdProblem &p, float *dq, float *dk, float *dv, int nsplit,
+                               int tps, hipStream_t stream);
 hipError_t launch_naive(const Problem &p, void *s_ws, void *p_ws, hipStream_t stream);
 
 }  // namespace fa

@@ -223,7 +223,7 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
  * dk and dv.  Results are bitwise identical from run to run; nsplit = 1 gives fa_bwd's.
  *
  *   all arguments but workspace and nsplit   as for fa_bwd.
- *   dtype      FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_DTYPE).
+ *   dtype      as for fa_bwd (FA_F32: d = 64 or 128).
  *   nsplit     1 .. FA_MAX_SPLIT (else FA_ERR_SHAPE).
  *   workspace  fa_bwd_split_workspace_bytes(B, H, N, d, dtype, nsplit) bytes of device
  *              memory, 256-byte aligned: fa_bwd's workspace followed by 3 nsplit
@@ -236,8 +236,8 @@ int fa_bwd_split(const void *q, const void *k, const void *v, const float *o, co
                  int B, int H, int N, int d, float scale, int dtype, void *stream);
 
 /* Workspace bytes of fa_bwd_split: fa_bwd_workspace_bytes(B, H, N, d, dtype) plus
- * 3 * nsplit * B * H * N * d float32 values rounded up to 256 bytes.  0 for FA_F32, an
- * unsupported d, negative sizes or nsplit outside 1 .. FA_MAX_SPLIT; SIZE_MAX if the
+ * 3 * nsplit * B * H * N * d float32 values rounded up to 256 bytes.  0 for an
+ * unsupported dtype or d, negative sizes or nsplit outside 1 .. FA_MAX_SPLIT; SIZE_MAX if the
  * size does not fit a size_t. */
 size_t fa_bwd_split_workspace_bytes(int B, int H, int N, int d, int dtype, int nsplit);
 

@@ -183,7 +183,7 @@ def test_bwd_split_arguments_and_sizes(lib):
     def call(dtype=1, d=64, ws=0x8000, nsplit=2, N=128, dout=0x9000):
         return lib.fa_bwd_split(A, B_, C_, O_, L_, dout, 0xa000, 0xb000, 0xc000, ws, nsplit,
                                 1, 1, N, d, 0.125, dtype, None)
-    assert call(dtype=0) == 4          # fp32 inputs: no split backward
+    assert call(dtype=0, d=256) == 3   # fp32 inputs at d = 256: no backward kernel
     assert call(d=96) == 3
     assert call(nsplit=0) == 2 and call(nsplit=65) == 2
     assert call(ws=0) == 7 and call(ws=0x8010) == 7
@@ -194,7 +194,9 @@ def test_bwd_split_arguments_and_sizes(lib):
     assert lib.fa_bwd_split_workspace_bytes(1, 2, 100, 64, 2, 4) == base + 3 * 4 * 2 * 100 * 64 * 4
     assert lib.fa_bwd_split_workspace_bytes(1, 1, 3, 64, 1, 1) == (
         lib.fa_bwd_workspace_bytes(1, 1, 3, 64, 1) + 2304)
-    assert lib.fa_bwd_split_workspace_bytes(1, 1, 3, 64, 0, 2) == 0
+    assert lib.fa_bwd_split_workspace_bytes(1, 1, 3, 64, 0, 2) == (
+        lib.fa_bwd_workspace_bytes(1, 1, 3, 64, 0) + 4608)             # fp32: no dO copy
+    assert lib.fa_bwd_split_workspace_bytes(1, 1, 3, 256, 0, 2) == 0
     assert lib.fa_bwd_split_workspace_bytes(1, 1, 3, 64, 1, 0) == 0
     s = lib.fa_bwd_split_suggest
     assert s(1, 1, 16384, 128, 256) == 4     # 128 workgroups of 128 rows (4: measured best)

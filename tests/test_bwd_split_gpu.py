@@ -37,6 +37,8 @@ def run(x, g_np, dtype, scale, nsplit):
     (1, 1, 333, 256, "bf16", 2),     # d = 256: dV and dK in two launches, both split
     (2, 1, 129, 128, "f16", 8),      # more ranges than tiles: three run
     (1, 1, 64, 64, "bf16", 2),       # one tile: one range runs
+    (1, 1, 300, 64, "f32", 3),       # fp32 inputs (fp32 matrix cores)
+    (1, 2, 200, 128, "f32", 2),
 ])
 def test_bwd_split_small_full(B, H, N, d, dtype, nsplit):
     scale = float(np.float32(1.0 / math.sqrt(d)))
