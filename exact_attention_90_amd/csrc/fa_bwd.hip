@@ -626,11 +626,6 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
 }
 
 // ------------------------------------------------------------------------------------
-template <typename KernelT>
-static hipError_t allow_lds_bwd(KernelT kernel, int bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
 
 // nsplit ranges of tps streamed tiles each; dq, dk, dv receive nsplit slots of B H N d
 // floats (with nsplit = 1 they are the gradients themselves)
@@ -656,8 +651,9 @@ static hipError_t run_bwd(const BwdProblem &p, float *dq, float *dk, float *dv, 
   // dK and dV: one launch, or (d = 256) one for dV and one for dK
   auto dkdv = [&](auto what) -> hipError_t {
     auto kern = fa_bwd_dkdv_kernel<D, BF16, WAVES, decltype(what)::value>;
-    static const hipError_t attr = allow_lds_bwd(kern, C::LDS);
-    (void)attr;
+    const hipError_t ea =
+        allow_lds_on_device<fa_bwd_dkdv_kernel<D, BF16, WAVES, decltype(what)::value>>(C::LDS);
+    if (ea != hipSuccess) return ea;
     hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
                        static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                        static_cast<const uint16_t *>(p.v), dO16, p.ws_lse2, p.ws_d, dk, dv,
@@ -676,8 +672,8 @@ static hipError_t run_bwd(const BwdProblem &p, float *dq, float *dk, float *dv, 
   }
   {
     auto kern = fa_bwd_dq_kernel<D, BF16, WAVES>;
-    static const hipError_t attr = allow_lds_bwd(kern, C::LDS);
-    (void)attr;
+    const hipError_t ea = allow_lds_on_device<fa_bwd_dq_kernel<D, BF16, WAVES>>(C::LDS);
+    if (ea != hipSuccess) return ea;
     hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
                        static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                        static_cast<const uint16_t *>(p.v), dO16, p.ws_lse2, p.ws_d, dq, p.N,

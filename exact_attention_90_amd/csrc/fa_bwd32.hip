@@ -329,9 +329,8 @@ static hipError_t run_bwd32(const BwdProblem &p, float *dq, float *dk, float *dv
               *v = static_cast<const float *>(p.v);
   {
     auto kern = fa_bwd32_dkdv_kernel<D>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    (void)attr;
+    const hipError_t ea = allow_lds_on_device<fa_bwd32_dkdv_kernel<D>>(C::LDS);
+    if (ea != hipSuccess) return ea;
     hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream, q, k, v, p.dout, p.ws_lse2,
                        p.ws_d, dk, dv, p.N, nb, G, c, p.scale, nsplit, tps);
     hipError_t e = hipGetLastError();
@@ -339,9 +338,8 @@ static hipError_t run_bwd32(const BwdProblem &p, float *dq, float *dk, float *dv
   }
   {
     auto kern = fa_bwd32_dq_kernel<D>;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, C::LDS);
-    (void)attr;
+    const hipError_t ea = allow_lds_on_device<fa_bwd32_dq_kernel<D>>(C::LDS);
+    if (ea != hipSuccess) return ea;
     hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream, q, k, v, p.dout, p.ws_lse2,
                        p.ws_d, dq, p.N, nb, G, c, p.scale, nsplit, tps);
   }

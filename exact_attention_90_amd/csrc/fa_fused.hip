@@ -620,11 +620,6 @@ __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
 }
 
 // ------------------------------------------------------------------------------------
-template <typename KernelT>
-static hipError_t allow_lds(KernelT kernel, int bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
 
 // Waves per workgroup of the 16-bit kernel: at d = 128, eight waves (256 query rows)
 // halve the K/V tile loads and the bfloat16 widening per query row; at d = 64 the
@@ -640,9 +635,8 @@ static hipError_t run16(const Problem &p, float *o, float *lse, int nsplit, int 
                         hipStream_t stream) {
   using C = Cfg16<D, WAVES>;
   auto kern = fa_fwd16_kernel<D, BF16, WAVES>;
-  // raise the dynamic-LDS cap once; a refusal surfaces as a launch error below
-  static const hipError_t attr = allow_lds(kern, C::LDS);
-  (void)attr;
+  const hipError_t ea = allow_lds_on_device<fa_fwd16_kernel<D, BF16, WAVES>>(C::LDS);
+  if (ea != hipSuccess) return ea;
   const int nqt = (p.N + C::BM - 1) / C::BM;
   const int G = nqt * p.B * p.H * nsplit;
   const float c = p.scale * kLog2e;
@@ -665,9 +659,8 @@ static hipError_t run32(const Problem &p, float *o, float *lse, int nsplit, int 
                         hipStream_t stream) {
   using C = Cfg32<D>;
   auto kern = fa_fwd32_kernel<D>;
-  // raise the dynamic-LDS cap once; a refusal surfaces as a launch error below
-  static const hipError_t attr = allow_lds(kern, C::LDS);
-  (void)attr;
+  const hipError_t ea = allow_lds_on_device<fa_fwd32_kernel<D>>(C::LDS);
+  if (ea != hipSuccess) return ea;
   const int nqt = (p.N + C::BM - 1) / C::BM;
   const int G = nqt * p.B * p.H * nsplit;
   const float c = p.scale * kLog2e;

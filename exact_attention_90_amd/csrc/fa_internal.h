@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fa {
 
 enum Dtype { kF32 = 0, kF16 = 1, kBF16 = 2 };
@@ -39,6 +41,24 @@ struct BwdProblem {
   float scale;
   int dtype;
 };
+
+// Raises kernel Kern's dynamic-LDS limit to `bytes` on the current device, once per
+// device (ids 0..63; beyond that on every call) and process: the limit is a per-device
+// attribute, so a process that uses several GPUs sets it on each.  A failure is
+// returned and nothing is remembered, so the next call tries again.
+template <auto Kern>
+inline hipError_t allow_lds_on_device(int bytes) {
+  static std::atomic<uint64_t> done{0};
+  int dev = 0;
+  const hipError_t g = hipGetDevice(&dev);
+  if (g != hipSuccess) return g;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(Kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 hipError_t launch_fused(const Problem &p, hipStream_t stream);
 // nsplit key ranges of kps keys into the partial buffers (opart: nsplit
