@@ -29,7 +29,8 @@
  *     nothing is launched and outputs are untouched.
  *   - NaN or Inf inside q, k or v is not checked; it propagates to the outputs.
  *   - All entry points are thread-safe; the library keeps no mutable state other
- *     than a per-thread copy of the last HIP error code.
+ *     than a per-thread copy of the last HIP error code and, per kernel, an atomic
+ *     record of the devices on which its dynamic-LDS limit has been raised.
  */
 #ifndef EXACT_ATTENTION_90_AMD_FA_H
 #define EXACT_ATTENTION_90_AMD_FA_H
