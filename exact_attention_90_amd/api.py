@@ -41,12 +41,31 @@ def _check_inputs(q, k, v):
         raise ValueError("q, k, v must be on one device")
 
 
+def _on_device(name, t, q):
+    """Every caller-supplied buffer must be a tensor on q's device: a host pointer handed
+    to a kernel as a device address would fault the GPU."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != q.device:
+        raise ValueError(f"{name} must be on {q.device} (got {t.device})")
+
+
+def _workspace(name, ws, q, nbytes):
+    _on_device(name, ws, q)
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"{name} too small: {ws.numel() * ws.element_size()} < {nbytes} bytes")
+
+
 def _outputs(q, out, lse):
     B, H, N, d = q.shape
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _on_device("out", out, q)
+    _on_device("lse", lse, q)
     if out.dtype != torch.float32 or out.shape != q.shape or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 tensor shaped like q")
     if lse.dtype != torch.float32 or lse.shape != q.shape[:3] or not lse.is_contiguous():
@@ -102,8 +121,7 @@ def fwd_split(q, k, v, nsplit: int | None = None, scale: float | None = None, ou
     nbytes = split_workspace_bytes(B, H, N, d, nsplit)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
-    if workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError("split workspace too small")
+    _workspace("split workspace", workspace, q, nbytes)
     lib = _lib.load()
     rc = lib.fa_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr(), workspace.data_ptr(), int(nsplit), B, H, N, d, scale,
@@ -132,8 +150,8 @@ def naive_fwd(q, k, v, scale: float | None = None, out=None, lse=None, workspace
         workspace = (torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device),
                      torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device))
     s_ws, p_ws = workspace
-    if s_ws.numel() * s_ws.element_size() < nbytes or p_ws.numel() * p_ws.element_size() < nbytes:
-        raise ValueError("naive workspace too small")
+    _workspace("naive S workspace", s_ws, q, nbytes)
+    _workspace("naive P workspace", p_ws, q, nbytes)
     lib = _lib.load()
     rc = lib.fa_naive_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                           lse.data_ptr(), s_ws.data_ptr(), p_ws.data_ptr(), B, H, N, d, scale,
@@ -165,14 +183,14 @@ def bwd(q, k, v, o, lse, dout, scale: float | None = None, workspace=None, grads
     if grads is None:
         grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
     dq, dk, dv = grads
-    for t in grads:
+    for name, t in zip(("dq", "dk", "dv"), grads):
+        _on_device(name, t, q)
         if t.dtype != torch.float32 or t.shape != q.shape or not t.is_contiguous():
             raise ValueError("grads must be contiguous float32 tensors shaped like q")
     nbytes = bwd_workspace_bytes(B, H, N, d, q.dtype)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
-    if workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError("backward workspace too small")
+    _workspace("backward workspace", workspace, q, nbytes)
     lib = _lib.load()
     rc = lib.fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
@@ -208,14 +226,14 @@ def bwd_split(q, k, v, o, lse, dout, nsplit: int | None = None, scale: float | N
     if grads is None:
         grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
     dq, dk, dv = grads
-    for t in grads:
+    for name, t in zip(("dq", "dk", "dv"), grads):
+        _on_device(name, t, q)
         if t.dtype != torch.float32 or t.shape != q.shape or not t.is_contiguous():
             raise ValueError("grads must be contiguous float32 tensors shaped like q")
     nbytes = bwd_split_workspace_bytes(B, H, N, d, q.dtype, nsplit)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
-    if workspace.numel() * workspace.element_size() < nbytes:
-        raise ValueError("split backward workspace too small")
+    _workspace("split backward workspace", workspace, q, nbytes)
     lib = _lib.load()
     rc = lib.fa_bwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                           lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),

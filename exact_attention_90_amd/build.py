@@ -16,13 +16,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.cpp", "fa_fused.hip", "fa_naive.hip", "fa_bwd.hip", "fa_bwd32.hip"]
+SOURCES = ["fa_api.cpp", "fa_fused.hip", "fa_fwd16.hip", "fa_fwd16_d128.hip", "fa_naive.hip",
+           "fa_bwd.hip", "fa_bwd32.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of every device code object.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-file code-generation choices (none at present).
-FILE_FLAGS = {}
+# Per-file code-generation choices: the d = 128 forward kernel takes its S products in
+# vector-register form (its P V products accumulate in AGPRs through assembly).
+FILE_FLAGS = {"fa_fwd16_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

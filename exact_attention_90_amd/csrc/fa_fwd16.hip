@@ -1,0 +1,25 @@
+// Instantiations of the 16-bit fused forward kernel for d = 64 and d = 256, and the
+// dispatch over head sizes (d = 128 is compiled in fa_fwd16_d128.hip).  Both use four
+// 32-row waves per workgroup: at d = 64 the softmax dominates and three waves per SIMD
+// schedule best; at d = 256 one 32-row wave already needs more than half of a SIMD's
+// registers.
+#include "fa_fwd16.hpp"
+
+namespace fa {
+
+hipError_t launch_fwd16(const Problem &p, float *o, float *lse, int nsplit, int kps,
+                        hipStream_t stream) {
+  const bool bf16 = p.dtype == kBF16;
+  switch (p.d) {
+    case 256:
+      return bf16 ? run16<256, true, 4, 1>(p, o, lse, nsplit, kps, stream)
+                  : run16<256, false, 4, 1>(p, o, lse, nsplit, kps, stream);
+    case 128:
+      return launch_fwd16_d128(p, o, lse, nsplit, kps, stream);
+    default:
+      return bf16 ? run16<64, true, 4, 1>(p, o, lse, nsplit, kps, stream)
+                  : run16<64, false, 4, 1>(p, o, lse, nsplit, kps, stream);
+  }
+}
+
+}  // namespace fa

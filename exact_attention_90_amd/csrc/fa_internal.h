@@ -61,6 +61,13 @@ inline hipError_t allow_lds_on_device(int bytes) {
 }
 
 hipError_t launch_fused(const Problem &p, hipStream_t stream);
+// the 16-bit kernels (binary16 / bfloat16 inputs): key ranges as in launch_fused_split,
+// written to o and lse (nsplit = 1, kps = N: the attention itself); d = 128 lives in
+// its own compilation unit
+hipError_t launch_fwd16(const Problem &p, float *o, float *lse, int nsplit, int kps,
+                        hipStream_t stream);
+hipError_t launch_fwd16_d128(const Problem &p, float *o, float *lse, int nsplit, int kps,
+                             hipStream_t stream);
 // nsplit key ranges of kps keys into the partial buffers (opart: nsplit
 // slots of B H N d floats, lpart: nsplit slots of B H N floats), then merged into p.o, p.lse
 hipError_t launch_fused_split(const Problem &p, float *opart, float *lpart, int nsplit,

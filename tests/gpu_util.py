@@ -77,6 +77,22 @@ def sample_rows(B, H, N, per_head=24, heads=12, seed=0):
     return np.array(sorted(set(rows)), np.int64)
 
 
+def spread_rows(B, H, N, count, seed=0):
+    """At least `count` distinct row indices (b*H + h)*N + i over every head: each head's
+    rows 0, 1, N-2, N-1 and its 64-row tile edges, the rest drawn at random, sorted."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    nh = B * H
+    per = max(4, -(-count // nh))
+    rows = []
+    for hd in range(nh):
+        ii = {0, 1, N - 2, N - 1} | set(range(0, N, 64)) | set(range(63, N, 64))
+        ii = {i for i in ii if 0 <= i < N}
+        while len(ii) < min(per, N):
+            ii.update(int(i) for i in rng.integers(0, N, size=min(per, N) - len(ii)))
+        rows.extend(hd * N + i for i in sorted(ii))
+    return np.array(sorted(set(rows)), np.int64)
+
+
 def full_case(B, H, N, d, dtype, seed, mult=1.0, scale=None, path="fused", x=None):
     """Run a whole small problem on the GPU and the oracle; return metrics."""
     scale = 1.0 / math.sqrt(d) if scale is None else scale

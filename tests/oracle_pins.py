@@ -91,6 +91,74 @@ def pin_brute_force(cases=None):
                 assert err_l <= 1e-12, f"brute force LSE mismatch {err_l:.3e} ({dtype},{N},{d})"
 
 
+# ------------------------------------------------------ storage-format widening
+def pin_storage_widening_every_pattern():
+    """Every finite binary16 and bfloat16 bit pattern (subnormals and signed zeros
+    included) reaches the arithmetic as the value a library gives it.  With Q = 0 every
+    score is 0, so each query row's O is the plain mean of the V rows; with the same
+    pattern in every V row that mean is the pattern's value exactly.  The reference
+    values come from numpy's float16 and torch's bfloat16 conversions to float64."""
+    import torch
+
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    for dtype in ("f16", "bf16"):
+        finite = (allbits & 0x7F80) != 0x7F80 if dtype == "bf16" else (allbits & 0x7C00) != 0x7C00
+        bits = allbits[finite]
+        if dtype == "f16":
+            ref = bits.view(np.float16).astype(np.float64)
+        else:
+            ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(
+                torch.float64).numpy()
+        d = 512
+        pad = (-len(bits)) % d
+        bits = np.concatenate([bits, np.zeros(pad, np.uint16)])
+        ref = np.concatenate([ref, np.zeros(pad)])
+        H = len(bits) // d
+        N = 2  # two identical key rows: O = (v + v) / 2 = v
+        v = np.ascontiguousarray(np.broadcast_to(bits.reshape(1, H, 1, d), (1, H, N, d)))
+        q = np.zeros((1, H, N, d), np.uint16)
+        k = np.ascontiguousarray(v[:, :, ::-1])  # any keys: Q = 0 makes every score 0
+        o, lse = oracle.attention(q, k, v, dtype, 0.5)
+        want = np.broadcast_to(ref.reshape(1, H, 1, d), o.shape)
+        bad = np.flatnonzero(o.reshape(-1) != want.reshape(-1))
+        assert bad.size == 0, (f"{dtype}: {bad.size} patterns widened wrongly, e.g. element "
+                               f"{bad[0]}: {o.reshape(-1)[bad[0]]!r} vs {want.reshape(-1)[bad[0]]!r}")
+        assert np.all(lse == math.log(N)), f"{dtype}: LSE of all-zero scores is not ln N"
+    # subnormal binary16 values enter the scores exactly too: q = 2^-24 (the smallest
+    # subnormal) times k = 2^15 gives 2^-9 per column, 2^-7 over four columns
+    q = np.full((1, 1, 1, 4), 0x0001, np.uint16)
+    k = np.full((1, 1, 1, 4), np.float16(2.0**15).view(np.uint16), np.uint16)
+    v = np.full((1, 1, 1, 4), np.float16(1.0).view(np.uint16), np.uint16)
+    s, _, _, _ = oracle.head_steps(q, k, v, "f16", 1.0)
+    assert s[0, 0] == 2.0**-7, f"subnormal query score {s[0, 0]!r} != 2^-7"
+
+
+# ------------------------------------------------------------ the rows= entry
+def pin_selected_rows_match_brute_force():
+    """oracle.attention(rows=...) on unsorted rows spanning several heads (duplicates,
+    first and last rows of heads) returns, in the order asked, each row's brute-force
+    result."""
+    B, H, N, d = 2, 2, 21, 8
+    rows = np.array([83, 0, 20, 21, 22, 41, 42, 83, 5, 62, 63, 20, 0, 70, 41], np.int64)
+    for dtype in ("f32", "f16", "bf16"):
+        x = make_qkv(B, H, N, d, dtype, seed=7, mult=1.3)
+        qf, kf, vf = (_f64(x[n], dtype) for n in "qkv")
+        scale = 0.3
+        o, lse = oracle.attention(x["q"], x["k"], x["v"], dtype, scale, rows=rows)
+        assert o.shape == (len(rows), d) and lse.shape == (len(rows),)
+        brute = {}
+        for r_i, g in enumerate(rows):
+            hd, i = divmod(int(g), N)
+            if hd not in brute:
+                b, h = divmod(hd, H)
+                brute[hd] = _brute_fsum(qf[b, h], kf[b, h], vf[b, h], scale)
+            Ob, Lb = brute[hd]
+            err_o = np.abs(o[r_i] - Ob[i]).max() / max(1.0, np.abs(vf).max())
+            err_l = abs(lse[r_i] - Lb[i]) / max(1.0, abs(Lb[i]))
+            assert err_o <= 1e-12 and err_l <= 1e-12, (
+                f"{dtype} row {g} (position {r_i}): O err {err_o:.3e}, LSE err {err_l:.3e}")
+
+
 # ----------------------------------------------------------- library routines
 def pin_scipy_softmax_logsumexp():
     """S equals scale*QK^T (numpy matmul), P equals scipy softmax(S), LSE equals logsumexp(S)."""
@@ -363,6 +431,8 @@ def pin_bwd_invariants():
 
 ALL_PINS = [
     pin_brute_force,
+    pin_storage_widening_every_pattern,
+    pin_selected_rows_match_brute_force,
     pin_scipy_softmax_logsumexp,
     pin_rows_sum_to_one,
     pin_zero_query,

@@ -13,7 +13,7 @@ import pytest
 import oracle
 from synth.configs import PAGE_WORKLOADS, WORKLOADS
 from synth.inputs import make_qkv, quantize, to_float32
-from tests.gpu_util import (assert_parity, full_case, metrics, run, sample_rows, say,
+from tests.gpu_util import (assert_parity, full_case, metrics, run, say, spread_rows,
                             to_device)
 
 pytestmark = pytest.mark.gpu
@@ -144,23 +144,47 @@ def test_bitwise_deterministic():
         assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
 
 
-# ---- the named workloads at full size, sampled rows -----------------------------------
-@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
-def test_workload_full_size_sampled(name):
-    w = WORKLOADS[name]
-    scale32 = float(np.float32(w.scale))
-    say(f"{name}: generating {w.short()}")
-    x = make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.mult)
-    say(f"{name}: fused kernel")
-    o, lse = run("fused", to_device(x, w.dtype), scale32)
-    rows = sample_rows(w.B, w.H, w.N)
-    o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], w.dtype, scale32, rows=rows)
+# ---- the named workloads at full size ----------------------------------------------
+def _compare_rows(name, w, o, lse, x, rows):
+    """Oracle on `rows` (None: every row) against the kernel's output."""
     import torch
 
-    idx = torch.from_numpy(rows).to(o.device)
-    o_s = o.reshape(-1, w.d).index_select(0, idx).cpu().numpy()
-    l_s = lse.reshape(-1).index_select(0, idx).cpu().numpy()
+    scale32 = float(np.float32(w.scale))
+    say(f"{name}: oracle on {'every row' if rows is None else f'{len(rows)} rows'}")
+    o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], w.dtype, scale32, rows=rows)
+    if rows is None:
+        o_s, l_s = o.cpu().numpy(), lse.cpu().numpy()
+    else:
+        idx = torch.from_numpy(rows).to(o.device)
+        o_s = o.reshape(-1, w.d).index_select(0, idx).cpu().numpy()
+        l_s = lse.reshape(-1).index_select(0, idx).cpu().numpy()
     m = metrics(o_s, l_s, o_ref, lse_ref)
     say(f"{name}: {m}")
     assert_parity(m, w.dtype, where=name)
-    assert bool(np.isfinite(o.cpu().numpy()).all())
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+
+
+def _run_workload(name):
+    w = WORKLOADS[name]
+    say(f"{name}: generating {w.short()}")
+    x = make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.mult)
+    say(f"{name}: fused kernel")
+    o, lse = run("fused", to_device(x, w.dtype), float(np.float32(w.scale)))
+    return w, x, o, lse
+
+
+@pytest.mark.parametrize("name", ["c2", "c4"])
+def test_workload_every_row(name):
+    # the whole output of the fp16 workloads against the oracle
+    w, x, o, lse = _run_workload(name)
+    _compare_rows(name, w, o, lse, x, None)
+
+
+@pytest.mark.parametrize("name,nrows", [("c3", 120_000), ("c5", 100_000)])
+def test_workload_many_rows(name, nrows):
+    # at least 1e5 rows spread over every head: each head's first and last rows, the
+    # edges of its query tiles and random rows
+    w, x, o, lse = _run_workload(name)
+    rows = spread_rows(w.B, w.H, w.N, nrows, seed=w.seed)
+    assert len(rows) >= nrows
+    _compare_rows(name, w, o, lse, x, rows)

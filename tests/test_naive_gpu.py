@@ -21,6 +21,7 @@ NAIVE_BF16_LSE_REL = 3e-3
     (1, 1, 128, 64, "f32"), (2, 2, 333, 128, "f16"), (1, 2, 300, 64, "f16"),
     (1, 3, 200, 128, "f32"), (2, 2, 333, 128, "bf16"), (1, 2, 257, 64, "bf16"),
     (1, 1, 1, 64, "f16"), (1, 2, 64, 128, "bf16"),
+    (1, 2, 130, 256, "f32"), (1, 2, 130, 256, "f16"), (1, 2, 130, 256, "bf16"),
 ])
 def test_naive_small_full(B, H, N, d, dtype):
     m, _, _ = full_case(B, H, N, d, dtype, seed=N + 3 * d, path="naive")
@@ -36,3 +37,33 @@ def test_naive_matches_fused_closely_fp32():
     m1, x, (o1, l1) = full_case(2, 2, 300, 64, "f32", seed=4, path="naive")
     m2, _, (o2, l2) = full_case(2, 2, 300, 64, "f32", seed=4, path="fused", x=x)
     assert np.abs(o1.cpu().numpy() - o2.cpu().numpy()).max() <= 2e-5
+
+
+def test_naive_headline_size_sampled():
+    # the size the contrast path is measured at (bf16 B8 H32 N4096 d128): every S and P
+    # offset is past 2^31 elements for the later heads; 10^4 rows over every head
+    import math
+
+    import oracle
+    import torch
+    from synth.configs import WORKLOADS
+    from synth.inputs import make_qkv
+    from tests.gpu_util import metrics, run, say, spread_rows, to_device
+
+    w = WORKLOADS["c3"]
+    scale32 = float(np.float32(1.0 / math.sqrt(w.d)))
+    say(f"naive c3: generating {w.short()}")
+    x = make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.mult)
+    say("naive c3: three kernels with 2 x 8.6 GB workspaces")
+    o, lse = run("naive", to_device(x, w.dtype), scale32)
+    rows = spread_rows(w.B, w.H, w.N, 10_000, seed=31)
+    assert rows.max() == w.B * w.H * w.N - 1
+    say(f"naive c3: oracle on {len(rows)} rows")
+    o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], w.dtype, scale32, rows=rows)
+    idx = torch.from_numpy(rows).to(o.device)
+    m = metrics(o.reshape(-1, w.d).index_select(0, idx).cpu().numpy(),
+                lse.reshape(-1).index_select(0, idx).cpu().numpy(), o_ref, lse_ref)
+    say(f"naive c3: {m}")
+    assert m["cosine"] >= 0.999
+    assert_parity(m, "bf16", max_abs=NAIVE_BF16_MAX_ABS, where="naive c3",
+                  lse_rel=NAIVE_BF16_LSE_REL)

@@ -33,6 +33,9 @@ MUTANTS = [
     ("mag = ldexp((double)(f | 0x400), e - 25);", "mag = ldexp((double)(f | 0x400), e - 24);",
      "binary16 exponent bias off by one"),
     ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;", "bfloat16 widening shift"),
+    ("mag = ldexp((double)f, -24);", "mag = ldexp((double)f, -23);", "binary16 subnormals doubled"),
+    ("                int64_t g = rows ? rows[r] : r;",
+     "                int64_t g = rows ? rows[r0] : r;", "selected rows all take the group's first query"),
     ("double alpha = exp(m - m_ij);", "double alpha = exp(m_ij - m);", "online rescale sign"),
     ("Oi[t] *= alpha;", "Oi[t] *= 1.0;", "online O rescale dropped"),
     ("l = alpha * l + rowsum;", "l = l + rowsum;", "online l rescale dropped"),
