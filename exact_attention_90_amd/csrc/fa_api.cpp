@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -125,28 +126,94 @@ size_t fa_fwd_split_workspace_bytes(int B, int H, int N, int d, int nsplit) {
   return (size_t)t;
 }
 
+}  // extern "C"
+
+namespace {
+// Checks of fa_fwd_split other than its workspace; *empty: nothing to compute.  Gives
+// the ranges: kps keys each (whole 64-key tiles), `used` of them (ranges that would
+// start past N are dropped).
+int split_check(const void *q, const void *k, const void *v, const float *o, const float *lse,
+                int nsplit, int B, int H, int N, int d, float scale, int dtype, bool *empty,
+                int *kps, int *used) {
+  int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, empty);
+  if (rc != FA_OK) return rc;
+  if (nsplit < 1 || nsplit > FA_MAX_SPLIT) return FA_ERR_SHAPE;
+  if (*empty) return FA_OK;
+  const int tiles = (N + 63) / 64;
+  *kps = (tiles + nsplit - 1) / nsplit * 64;
+  *used = (N + *kps - 1) / *kps;
+  const int64_t qtiles = (int64_t(N) + fa::kFusedBM - 1) / fa::kFusedBM;
+  if (int64_t(B) * H * qtiles * *used > fa::kMaxGrid) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int split_launch(const void *q, const void *k, const void *v, float *o, float *lse, char *ws,
+                 int nsplit, int B, int H, int N, int d, float scale, int dtype, int kps,
+                 int used, void *stream) {
+  const SplitLayout L = split_layout(B, H, N, d, nsplit);
+  return hip_status(fa::launch_fused_split(
+      make_problem(q, k, v, o, lse, B, H, N, d, scale, dtype), reinterpret_cast<float *>(ws),
+      reinterpret_cast<float *>(ws + (size_t)L.lse), used, kps, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+// The allocation-free key split's scratch: FA_SCRATCH_BYTES of device memory per
+// device, held until the process ends.  In host code `scratch` names a host-side
+// stand-in, not device memory; the device address of each device's copy comes from
+// hipGetSymbolAddress and is kept per device.
+static __device__ __align__(256) unsigned char scratch[FA_SCRATCH_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::atomic<void *> g_scratch_addr[kScratchDevices];  // per device id; null until looked up
+
+// This device's scratch address (looked up once per device, with the device current).
+int scratch_address(void **addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  const bool cached = dev >= 0 && dev < kScratchDevices;
+  void *p = cached ? g_scratch_addr[dev].load(std::memory_order_acquire) : nullptr;
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr) return FA_ERR_HIP;
+    if (cached) g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *addr = p;
+  return FA_OK;
+}
+}  // namespace
+
+extern "C" {
+
 int fa_fwd_split(const void *q, const void *k, const void *v, float *o, float *lse,
                  void *workspace, int nsplit, int B, int H, int N, int d, float scale, int dtype,
                  void *stream) {
   bool empty = false;
-  int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
-  if (rc != FA_OK) return rc;
-  if (nsplit < 1 || nsplit > FA_MAX_SPLIT) return FA_ERR_SHAPE;
-  if (empty) return FA_OK;
+  int kps = 0, used = 0;
+  int rc = split_check(q, k, v, o, lse, nsplit, B, H, N, d, scale, dtype, &empty, &kps, &used);
+  if (rc != FA_OK || empty) return rc;
   if (!workspace || !aligned(workspace, 256)) return FA_ERR_WORKSPACE;
-  // ranges of whole 64-key tiles; ranges that would start past N are dropped
-  const int tiles = (N + 63) / 64;
-  const int kps = (tiles + nsplit - 1) / nsplit * 64;
-  const int used = (N + kps - 1) / kps;
-  const int64_t qtiles = (int64_t(N) + fa::kFusedBM - 1) / fa::kFusedBM;
-  if (int64_t(B) * H * qtiles * used > fa::kMaxGrid) return FA_ERR_SHAPE;
   rc = device_ready();
   if (rc != FA_OK) return rc;
-  const SplitLayout L = split_layout(B, H, N, d, nsplit);
-  char *ws = static_cast<char *>(workspace);
-  return hip_status(fa::launch_fused_split(
-      make_problem(q, k, v, o, lse, B, H, N, d, scale, dtype), reinterpret_cast<float *>(ws),
-      reinterpret_cast<float *>(ws + (size_t)L.lse), used, kps, static_cast<hipStream_t>(stream)));
+  return split_launch(q, k, v, o, lse, static_cast<char *>(workspace), nsplit, B, H, N, d, scale,
+                      dtype, kps, used, stream);
+}
+
+int fa_fwd_split_noalloc(const void *q, const void *k, const void *v, float *o, float *lse,
+                         int nsplit, int B, int H, int N, int d, float scale, int dtype,
+                         void *stream) {
+  bool empty = false;
+  int kps = 0, used = 0;
+  int rc = split_check(q, k, v, o, lse, nsplit, B, H, N, d, scale, dtype, &empty, &kps, &used);
+  if (rc != FA_OK || empty) return rc;
+  if (fa_fwd_split_workspace_bytes(B, H, N, d, nsplit) > FA_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  void *ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != FA_OK) return rc;
+  return split_launch(q, k, v, o, lse, static_cast<char *>(ws), nsplit, B, H, N, d, scale, dtype,
+                      kps, used, stream);
 }
 
 size_t fa_naive_workspace_bytes(int B, int H, int N, int dtype) {
@@ -332,6 +399,7 @@ const char *fa_status_string(int status) {
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_WORKSPACE: return "workspace NULL or misaligned";
     case FA_ERR_HIP: return "HIP error (no device or launch failure)";
+    case FA_ERR_SCRATCH: return "problem needs more than the library's static scratch";
     default: return "unknown status";
   }
 }

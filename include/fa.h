@@ -59,7 +59,9 @@ enum fa_status {
     FA_ERR_SCALE = 5,     /* scale is not a finite number > 0 */
     FA_ERR_ALIGN = 6,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
     FA_ERR_WORKSPACE = 7, /* a workspace pointer is NULL or misaligned */
-    FA_ERR_HIP = 8        /* no usable HIP device, or a launch failed; see fa_last_hip_error */
+    FA_ERR_HIP = 8,       /* no usable HIP device, or a launch failed; see fa_last_hip_error */
+    FA_ERR_SCRATCH = 9    /* fa_fwd_split_noalloc: the problem needs more than FA_SCRATCH_BYTES
+                             of scratch */
 };
 
 /*
@@ -128,6 +130,33 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
 int fa_fwd_split(const void *q, const void *k, const void *v, float *o, float *lse,
                  void *workspace, int nsplit, int B, int H, int N, int d, float scale, int dtype,
                  void *stream);
+
+/* Bytes of the library's own static device scratch used by fa_fwd_split_noalloc. */
+#define FA_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * fa_fwd_split_noalloc - fa_fwd_split without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code being captured into
+ * a HIP graph, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The partial O_g and LSE_g go to a static device array of FA_SCRATCH_BYTES (64 MiB)
+ * that the library holds on every device it runs on until the process ends.  The call
+ * allocates and frees nothing (the array's device address is looked up once per device
+ * on the first call there).  The kernels and results are fa_fwd_split's: bitwise equal
+ * for the same arguments.
+ *
+ *   arguments  as for fa_fwd_split, minus workspace.
+ *
+ * Every call on one device shares that device's array, and a call may leave its
+ * contents there: calls that can overlap on one device (several streams, several host
+ * threads) race on it and must be serialised by the caller.  Nothing in the array needs
+ * to start at zero (every partial the merge reads is written first).
+ * Returns FA_OK, the error codes of fa_fwd_split, or FA_ERR_SCRATCH (before anything is
+ * enqueued) when fa_fwd_split_workspace_bytes(B, H, N, d, nsplit) > FA_SCRATCH_BYTES.
+ */
+int fa_fwd_split_noalloc(const void *q, const void *k, const void *v, float *o, float *lse,
+                         int nsplit, int B, int H, int N, int d, float scale, int dtype,
+                         void *stream);
 
 /*
  * fa_fwd_split_suggest - the number of key ranges for fa_fwd_split on a device with

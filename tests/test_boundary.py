@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings_and_version(lib):
-    for code in range(0, 9):
+    for code in range(0, 10):
         s = lib.fa_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.fa_status_string(99).decode() == "unknown status"
@@ -148,6 +148,24 @@ def test_split_rejects_bad_arguments(lib):
     assert split_call(lib, q=A + 8) == 6
     assert split_call(lib, B=2**20, H=2**10, N=2**12, nsplit=1) == 2   # grid limit
     assert split_call(lib, N=0, ws=0) == 0      # empty problem: nothing to launch
+
+
+def test_split_noalloc_rejects_before_any_launch(lib):
+    # the allocation-free key split checks like fa_fwd_split (minus the workspace) and
+    # refuses problems whose partials exceed the static scratch, all before touching a
+    # device (these pointers are never dereferenced)
+    def call(dtype=1, d=64, nsplit=2, B=1, H=1, N=128, q=A):
+        return lib.fa_fwd_split_noalloc(q, B_, C_, O_, L_, nsplit, B, H, N, d, 0.125, dtype, None)
+    assert call(dtype=5) == 4
+    assert call(d=96) == 3
+    assert call(nsplit=0) == 2 and call(nsplit=65) == 2
+    assert call(q=A + 8) == 6
+    assert call(N=0) == 0
+    assert _lib.FA_SCRATCH_BYTES == 64 << 20
+    # 4 ranges of 8 heads x 8192 rows at d = 128 need 4 x 65536 x 129 x 4 bytes > 64 MiB
+    assert lib.fa_fwd_split_workspace_bytes(1, 8, 8192, 128, 4) > _lib.FA_SCRATCH_BYTES
+    assert call(H=8, N=8192, d=128, nsplit=4) == 9
+    assert lib.fa_status_string(9).decode() == "problem needs more than the library's static scratch"
 
 
 def test_split_workspace_bytes(lib):
