@@ -25,7 +25,8 @@ STATUS = {
 }
 FA_SCRATCH_BYTES = 64 << 20
 # every symbol include/fa.h declares
-EXPORTS = ("fa_fwd", "fa_fwd_split", "fa_fwd_split_noalloc", "fa_fwd_split_suggest", "fa_fwd_split_workspace_bytes", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes",
+EXPORTS = ("fa_fwd", "fa_fwd_stats", "fa_fwd_stats_bytes", "fa_fwd_split",
+           "fa_fwd_split_noalloc", "fa_fwd_split_suggest", "fa_fwd_split_workspace_bytes", "fa_naive_fwd", "fa_naive_workspace_bytes", "fa_bwd", "fa_bwd_workspace_bytes",
            "fa_bwd_split", "fa_bwd_split_workspace_bytes", "fa_bwd_split_suggest",
            "fa_status_string", "fa_version", "fa_last_hip_error")
 
@@ -53,6 +54,10 @@ def load():
     lib.fa_fwd.restype = I
     lib.fa_fwd_split.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.fa_fwd_split.restype = I
+    lib.fa_fwd_stats.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P]
+    lib.fa_fwd_stats.restype = I
+    lib.fa_fwd_stats_bytes.argtypes = [I, I, I]
+    lib.fa_fwd_stats_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_split_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P]
     lib.fa_fwd_split_noalloc.restype = I
     lib.fa_fwd_split_suggest.argtypes = [I, I, I, I, I]

@@ -96,6 +96,23 @@ def fwd(q, k, v, scale: float | None = None, out=None, lse=None, stream=None):
     return out, lse
 
 
+def fwd_stats(q, k, v, scale: float | None = None, stream=None):
+    """fa_fwd in its statistics-recording form (validation): returns (o, lse, stats) with
+    stats float32 [B, H, N, ceil(N/64), 2]: per query row and 64-key block, the kernel's
+    running reference (base-2 units) and running row sum after that block."""
+    _check_inputs(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q, None, None)
+    stats = torch.empty((B, H, N, (N + 63) // 64, 2), dtype=torch.float32, device=q.device)
+    lib = _lib.load()
+    rc = lib.fa_fwd_stats(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), stats.data_ptr(), B, H, N, d, scale, _CODES[q.dtype],
+                          _stream(q, stream))
+    _lib.check(rc, "fa_fwd_stats")
+    return out, lse, stats
+
+
 def split_workspace_bytes(B: int, H: int, N: int, d: int, nsplit: int) -> int:
     return int(_lib.load().fa_fwd_split_workspace_bytes(B, H, N, d, nsplit))
 

@@ -90,6 +90,28 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_fwd_stats_bytes(int B, int H, int N) {
+  if (B < 0 || H < 0 || N < 0) return 0;
+  const unsigned __int128 n = (unsigned __int128)(uint64_t)B * (uint64_t)H * (uint64_t)N *
+                              (uint64_t)((N + 63) / 64) * 2 * sizeof(float);
+  if (n > (unsigned __int128)std::numeric_limits<size_t>::max())
+    return std::numeric_limits<size_t>::max();
+  return (size_t)n;
+}
+
+int fa_fwd_stats(const void *q, const void *k, const void *v, float *o, float *lse,
+                 float *stats, int B, int H, int N, int d, float scale, int dtype, void *stream) {
+  bool empty = false;
+  int rc = check_args(q, k, v, o, lse, B, H, N, d, scale, dtype, &empty);
+  if (rc != FA_OK || empty) return rc;
+  if (!stats || !aligned(stats, 16)) return FA_ERR_WORKSPACE;
+  if (fa_fwd_stats_bytes(B, H, N) == std::numeric_limits<size_t>::max()) return FA_ERR_SHAPE;
+  rc = device_ready();
+  if (rc != FA_OK) return rc;
+  return hip_status(fa::launch_fused_stats(make_problem(q, k, v, o, lse, B, H, N, d, scale, dtype),
+                                           stats, static_cast<hipStream_t>(stream)));
+}
+
 // Workspace of the key-split forward: nsplit slots of partial O (B H N d floats), then
 // nsplit slots of partial LSE (B H N floats), each part starting on a 256-byte boundary.
 namespace {

@@ -49,11 +49,13 @@ struct Cfg32 {
   static constexpr bool FENCE = D == 256;
 };
 
-template <int D>
+// STATS: the statistics-recording form (nsplit = 1): after every key tile each query
+// row's running max (base-2 units) and row sum go to ST, as in fa_fwd16_kernel.
+template <int D, bool STATS = false>
 __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
     const float *__restrict__ Q, const float *__restrict__ K, const float *__restrict__ V,
     float *__restrict__ O, float *__restrict__ LSE, int N, int nqt, int G, float c, int nsplit,
-    int kps) {
+    int kps, float *__restrict__ ST) {
   using C = Cfg32<D>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *const Ks = smem;
@@ -158,6 +160,18 @@ __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
       softmax_tile<C::SB, C::OB, true>(s, o, mc, l, c, nvalid, h);
     else
       softmax_tile<C::SB, C::OB, false>(s, o, mc, l, c, nvalid, h);
+    if constexpr (STATS) {
+      // a tile of 32 keys at d = 256: the record is per 64 keys, after every second tile
+      constexpr int TPR = 64 / C::BN;  // tiles per record
+      const float lt = pair_sum(l);
+      const int row = q0 + 32 * w + l32;
+      if ((kt % TPR == TPR - 1 || kt == nkt - 1) && h == 0 && row < N) {
+        const int ntr = (NK + 63) / 64;
+        float *p = ST + ((int64_t(bh) * N + row) * ntr + kt / TPR) * 2;
+        p[0] = mc;
+        p[1] = lt;
+      }
+    }
 
     // O^T += V^T P^T, one key pair per step: register r of block t holds, on lane half
     // h, key 32t + 8(r/4) + 4h + r%4; the V operand is that key's row, column 32e + l32
@@ -192,19 +206,20 @@ __global__ __launch_bounds__(256, 1) void fa_fwd32_kernel(
 
 // ------------------------------------------------------------------------------------
 
-template <int D>
+template <int D, bool STATS = false>
 static hipError_t run32(const Problem &p, float *o, float *lse, int nsplit, int kps,
-                        hipStream_t stream) {
+                        hipStream_t stream, float *stats = nullptr) {
   using C = Cfg32<D>;
-  auto kern = fa_fwd32_kernel<D>;
-  const hipError_t ea = allow_lds_on_device<fa_fwd32_kernel<D>>(C::LDS);
+  auto kern = fa_fwd32_kernel<D, STATS>;
+  const hipError_t ea = allow_lds_on_device<fa_fwd32_kernel<D, STATS>>(C::LDS);
   if (ea != hipSuccess) return ea;
   const int nqt = (p.N + C::BM - 1) / C::BM;
   const int G = nqt * p.B * p.H * nsplit;
   const float c = p.scale * kLog2e;
   hipLaunchKernelGGL(kern, dim3(G), dim3(256), C::LDS, stream,
                      static_cast<const float *>(p.q), static_cast<const float *>(p.k),
-                     static_cast<const float *>(p.v), o, lse, p.N, nqt, G, c, nsplit, kps);
+                     static_cast<const float *>(p.v), o, lse, p.N, nqt, G, c, nsplit, kps,
+                     stats);
   return hipGetLastError();
 }
 
@@ -223,6 +238,13 @@ hipError_t launch_fused(const Problem &p, hipStream_t stream) {
     default:
       return run32_any(p, p.o, p.lse, 1, p.N, stream);
   }
+}
+
+hipError_t launch_fused_stats(const Problem &p, float *stats, hipStream_t stream) {
+  if (p.dtype != kF32) return launch_fwd16(p, p.o, p.lse, 1, p.N, stream, stats);
+  return p.d == 256 ? run32<256, true>(p, p.o, p.lse, 1, p.N, stream, stats)
+         : p.d == 128 ? run32<128, true>(p, p.o, p.lse, 1, p.N, stream, stats)
+                      : run32<64, true>(p, p.o, p.lse, 1, p.N, stream, stats);
 }
 
 // ------------------------------------------------------------------------------------

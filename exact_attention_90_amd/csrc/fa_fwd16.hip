@@ -8,14 +8,26 @@
 namespace fa {
 
 hipError_t launch_fwd16(const Problem &p, float *o, float *lse, int nsplit, int kps,
-                        hipStream_t stream) {
+                        hipStream_t stream, float *stats) {
   const bool bf16 = p.dtype == kBF16;
+  if (stats != nullptr) {  // the statistics-recording form (nsplit = 1)
+    switch (p.d) {
+      case 256:
+        return bf16 ? run16<256, true, 4, 1, true>(p, o, lse, 1, p.N, stream, stats)
+                    : run16<256, false, 4, 1, true>(p, o, lse, 1, p.N, stream, stats);
+      case 128:
+        return launch_fwd16_d128(p, o, lse, 1, p.N, stream, stats);
+      default:
+        return bf16 ? run16<64, true, 4, 1, true>(p, o, lse, 1, p.N, stream, stats)
+                    : run16<64, false, 4, 1, true>(p, o, lse, 1, p.N, stream, stats);
+    }
+  }
   switch (p.d) {
     case 256:
       return bf16 ? run16<256, true, 4, 1>(p, o, lse, nsplit, kps, stream)
                   : run16<256, false, 4, 1>(p, o, lse, nsplit, kps, stream);
     case 128:
-      return launch_fwd16_d128(p, o, lse, nsplit, kps, stream);
+      return launch_fwd16_d128(p, o, lse, nsplit, kps, stream, nullptr);
     default:
       return bf16 ? run16<64, true, 4, 1>(p, o, lse, nsplit, kps, stream)
                   : run16<64, false, 4, 1>(p, o, lse, nsplit, kps, stream);

@@ -82,11 +82,15 @@ __device__ __forceinline__ void mfma_drain() {
 // the S products of both blocks and every V operand read feeds both P V products, which
 // halves the LDS operand bytes per flop; the two blocks' output accumulators then need
 // the matrix-core (AGPR) registers, and one wave runs per SIMD.
-template <int D, bool BF16, int WAVES, int RB>
+//
+// STATS: the statistics-recording form (validation only, nsplit = 1): after every key
+// tile t each query row's running max (base-2 units, c m) and row sum go to
+// ST[((b H + h) N + i) ceil(N/64) + t][0..1].  The other forms ignore ST.
+template <int D, bool BF16, int WAVES, int RB, bool STATS = false>
 __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int N,
-    int nqt, int G, float c, int nsplit, int kps) {
+    int nqt, int G, float c, int nsplit, int kps, float *__restrict__ ST) {
   using C = Cfg16<D, WAVES, RB>;
   constexpr int SB = C::SB, OB = C::OB, PU = C::PU, CPT = C::CPT;
   constexpr int NA = SB * C::KC;  // matrix-core steps of S^T = K Q^T per tile
@@ -371,6 +375,18 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   };
   // A step k's share: key-block-1 exponentials on steps 0 .. NEA-1, then (step NEA) the
   // last two operand blocks and l; O = alpha O on the steps that rebuild s[r][1]
+  // statistics form: the tile whose softmax the next A half completes, and the record of
+  // (c m, l) for block r once l includes it (both lanes of a row pair hold half of l)
+  int st_tile = 0;
+  auto record_stats = [&](int r) __attribute__((always_inline)) {
+    const float lt = pair_sum(l[r]);
+    const int row = q0 + 32 * (RB * w + r) + l32;
+    if (h == 0 && row < N) {
+      float *p = ST + ((int64_t(bh) * N + row) * nkt + st_tile) * 2;
+      p[0] = mc[r];
+      p[1] = lt;
+    }
+  };
   auto soft_a = [&](int k, int r, bool with_max = true) __attribute__((always_inline)) {
     if (k < NEA) exp_range(16 + k * 16 / NEA, 16 + (k + 1) * 16 / NEA, r);
     if (k == NEA) {
@@ -378,6 +394,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
       pack_u(3, r);
       l[r] = fmaf(l[r], alpha[r], rs[r]);
       if constexpr (LAZY) lp[r] = fmaf(lp[r], alpha[r], rp[r]);
+      if constexpr (STATS) record_stats(r);
     }
     if (EARLY_MAX && with_max && k >= KC + 2) max_a(k - KC - 2, r);
     if (!LAZY && k >= KC) {
@@ -509,6 +526,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
     char *kw = Ks + P * C::TILEB;                       // K_{j+2}
 
     // ---- A ----
+    st_tile = j;
     dma_v(vw, j + 1);
     dma_k(kw, j + 2);
     rescale_lazy();
@@ -563,6 +581,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // ---- last tile T = nkt - 1: the A share of its softmax, then its P V product ----
   {
     const int vb = v_base + (2 + ((nkt - 1) & 1)) * C::TILEB;
+    st_tile = nkt - 1;
     rescale_lazy();
 #pragma unroll
     for (int k = 0; k < NA; ++k)
@@ -594,19 +613,22 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
 // Launch of the 16-bit kernel with WAVES waves of RB 32-row query blocks each.
 // nsplit key ranges of kps keys each (the last may be shorter, none is empty); with
 // nsplit = 1 and kps = N the kernel writes the attention itself to o and lse
-template <int D, bool BF16, int WAVES, int RB>
+// STATS: the statistics-recording form, writing to stats (nsplit = 1).
+template <int D, bool BF16, int WAVES, int RB, bool STATS = false>
 inline hipError_t run16(const Problem &p, float *o, float *lse, int nsplit, int kps,
-                        hipStream_t stream) {
+                        hipStream_t stream, float *stats = nullptr) {
   using C = Cfg16<D, WAVES, RB>;
-  auto kern = fa_fwd16_kernel<D, BF16, WAVES, RB>;
-  const hipError_t ea = allow_lds_on_device<fa_fwd16_kernel<D, BF16, WAVES, RB>>(C::LDS);
+  auto kern = fa_fwd16_kernel<D, BF16, WAVES, RB, STATS>;
+  const hipError_t ea =
+      allow_lds_on_device<fa_fwd16_kernel<D, BF16, WAVES, RB, STATS>>(C::LDS);
   if (ea != hipSuccess) return ea;
   const int nqt = (p.N + C::BM - 1) / C::BM;
   const int G = nqt * p.B * p.H * nsplit;
   const float c = p.scale * kLog2e;
   hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
                      static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
-                     static_cast<const uint16_t *>(p.v), o, lse, p.N, nqt, G, c, nsplit, kps);
+                     static_cast<const uint16_t *>(p.v), o, lse, p.N, nqt, G, c, nsplit, kps,
+                     stats);
   return hipGetLastError();
 }
 

@@ -12,7 +12,10 @@
 namespace fa {
 
 hipError_t launch_fwd16_d128(const Problem &p, float *o, float *lse, int nsplit, int kps,
-                             hipStream_t stream) {
+                             hipStream_t stream, float *stats) {
+  if (stats != nullptr)
+    return p.dtype == kBF16 ? run16<128, true, 8, 1, true>(p, o, lse, 1, p.N, stream, stats)
+                            : run16<128, false, 8, 1, true>(p, o, lse, 1, p.N, stream, stats);
   return p.dtype == kBF16 ? run16<128, true, 8, 1>(p, o, lse, nsplit, kps, stream)
                           : run16<128, false, 8, 1>(p, o, lse, nsplit, kps, stream);
 }

@@ -63,11 +63,16 @@ inline hipError_t allow_lds_on_device(int bytes) {
 hipError_t launch_fused(const Problem &p, hipStream_t stream);
 // the 16-bit kernels (binary16 / bfloat16 inputs): key ranges as in launch_fused_split,
 // written to o and lse (nsplit = 1, kps = N: the attention itself); d = 128 lives in
-// its own compilation unit
+// its own compilation unit.  stats != nullptr selects the statistics-recording form
+// (nsplit = 1; see launch_fused_stats).
 hipError_t launch_fwd16(const Problem &p, float *o, float *lse, int nsplit, int kps,
-                        hipStream_t stream);
+                        hipStream_t stream, float *stats = nullptr);
 hipError_t launch_fwd16_d128(const Problem &p, float *o, float *lse, int nsplit, int kps,
-                             hipStream_t stream);
+                             hipStream_t stream, float *stats);
+// the fused forward in its statistics-recording form: besides O and LSE, every query
+// row's running max (base-2 units, scale log2(e) max s) and running row sum after every
+// 64-key tile, as float pairs [B H N][ceil(N / 64)][2]
+hipError_t launch_fused_stats(const Problem &p, float *stats, hipStream_t stream);
 // nsplit key ranges of kps keys into the partial buffers (opart: nsplit
 // slots of B H N d floats, lpart: nsplit slots of B H N floats), then merged into p.o, p.lse
 hipError_t launch_fused_split(const Problem &p, float *opart, float *lpart, int nsplit,

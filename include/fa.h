@@ -95,6 +95,32 @@ enum fa_status {
 int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, int B, int H, int N,
            int d, float scale, int dtype, void *stream);
 
+/*
+ * fa_fwd_stats - fa_fwd that also records the online-softmax statistics of every query
+ * row after every 64-key block, for validation: the second layer of the three-layer check
+ * in the CK/MI50 notes (section 4.1) compares each block's running max and running sum
+ * with the standard softmax, here with the CPU oracle's blockwise recurrences (MUSA
+ * guide, online-softmax recurrences m_new = max(m, max_j s_j), l_new = l e^(m - m_new) +
+ * sum_j e^(s_j - m_new)).  Same kernels as fa_fwd in a statistics-recording form; O and
+ * LSE are fa_fwd's.
+ *
+ *   q, k, v, o, lse, B, H, N, d, scale, dtype, stream   as for fa_fwd.
+ *   stats   caller-owned float32 device memory of fa_fwd_stats_bytes(B, H, N) bytes,
+ *           16-byte aligned (else FA_ERR_WORKSPACE): for row r = (b H + h) N + i and
+ *           block t = 0 .. ceil(N/64) - 1, stats[(r ceil(N/64) + t) 2 + 0] is the kernel's
+ *           running reference in base-2 units, log2(e) times the scaled score max over
+ *           keys 0 .. 64 t + 63 (at d = 256 for 16-bit inputs a lagging reference at most
+ *           8 below it, see the kernel), and stats[... + 1] the running sum of
+ *           exp2(log2(e) s_j - reference) over those keys.
+ * Returns FA_OK or an fa_status error code (as fa_fwd, plus FA_ERR_WORKSPACE).
+ */
+int fa_fwd_stats(const void *q, const void *k, const void *v, float *o, float *lse,
+                 float *stats, int B, int H, int N, int d, float scale, int dtype, void *stream);
+
+/* fa_fwd_stats_bytes - bytes of fa_fwd_stats' stats buffer: B H N ceil(N/64) 2 floats
+ * (0 for negative sizes, SIZE_MAX on overflow). */
+size_t fa_fwd_stats_bytes(int B, int H, int N);
+
 /* Largest number of key ranges fa_fwd_split accepts. */
 #define FA_MAX_SPLIT 64
 

@@ -168,6 +168,19 @@ def test_split_noalloc_rejects_before_any_launch(lib):
     assert lib.fa_status_string(9).decode() == "problem needs more than the library's static scratch"
 
 
+def test_stats_arguments_and_sizes(lib):
+    # the statistics-recording forward checks like fa_fwd, plus its stats buffer
+    def call(st=0x8000, dtype=1, d=64, N=128, q=A):
+        return lib.fa_fwd_stats(q, B_, C_, O_, L_, st, 1, 1, N, d, 0.125, dtype, None)
+    assert call(dtype=5) == 4 and call(d=96) == 3 and call(q=A + 8) == 6
+    assert call(st=0) == 7 and call(st=0x8004) == 7  # NULL or misaligned stats
+    assert call(N=0, st=0) == 0
+    # two floats per row and 64-key block
+    assert lib.fa_fwd_stats_bytes(1, 2, 333) == 2 * 333 * 6 * 2 * 4
+    assert lib.fa_fwd_stats_bytes(2, 3, 64) == 6 * 64 * 1 * 8
+    assert lib.fa_fwd_stats_bytes(-1, 1, 1) == 0
+
+
 def test_split_workspace_bytes(lib):
     # nsplit slots of partial O (d floats per row) and of partial LSE (one float per row),
     # each part rounded up to 256 bytes
