@@ -37,6 +37,9 @@ ALL_WORKLOADS = {**WORKLOADS, **HEADDIM_WORKLOADS}
 METRIC = "fwd attention TFLOP/s & % of bf16 MFMA peak, B8 H32 N4096 d128"
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}  # MI355X dense matrix-core peaks
 KERNEL_SOURCES = ("exact_attention_90_amd/csrc/fa_fused.hip",
+                  "exact_attention_90_amd/csrc/fa_fwd16.hpp",
+                  "exact_attention_90_amd/csrc/fa_fwd16.hip",
+                  "exact_attention_90_amd/csrc/fa_fwd16_d128.hip",
                   "exact_attention_90_amd/csrc/fa_softmax.hpp",
                   "exact_attention_90_amd/csrc/fa_device.hpp")
 # the backward kernels have their own hash (bench --pass bwd), so that a change to them
@@ -45,6 +48,29 @@ BWD_KERNEL_SOURCES = ("exact_attention_90_amd/csrc/fa_bwd.hip",
                       "exact_attention_90_amd/csrc/fa_softmax.hpp",
                       "exact_attention_90_amd/csrc/fa_device.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.md")
+# Frozen forward throughput (TFLOP/s) of each named workload, the reference a later change
+# is compared with: the line reports value / frozen as `vs_frozen` and warns below 0.95.
+# c3: the driver's own bench run of the eight-wave kernel (2.290 ms per call, 38.4 % of
+# peak); the others: this bench on the same kernel (the low end of the measured ranges).
+FROZEN_TFLOPS = {"c3": 960.4, "c2": 809.0, "c4": 840.0, "c5": 1043.0, "d256": 812.0}
+
+
+def host_cpu():
+    """The host CPU's model name (lscpu's 'Model name', from /proc/cpuinfo) and the number
+    of processors this process may run on."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count() or 0
+    return model, nproc
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
@@ -110,10 +136,13 @@ def cpu_baseline(x, w, o_gpu, lse_gpu, target_s: float):
                         (np.linalg.norm(og) * np.linalg.norm(o_ref))),
         "lse_rel": float((np.abs(lg - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)).max()),
     }
+    model, nproc = host_cpu()
     base = {
         "value": flops_row * len(rows) / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(oracle.num_threads()),
+        "cpu_model": model,
+        "nproc": nproc,
         "kind": "oracle",
         "sample": (f"{len(rows)} of {total} query rows of {w.name} ({w.short()}): rows "
                    f"0, {stride}, 2*{stride}, ... each against all N={w.N} keys; fp64 C "
@@ -316,7 +345,6 @@ def main() -> int:
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
-        "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic, all zeros" if args.zero_inputs else "synthetic",
@@ -341,6 +369,12 @@ def main() -> int:
         },
         "cpu_baseline": None,
     }
+    frozen = FROZEN_TFLOPS.get(w.name)
+    if frozen and args.path == "fused" and not args.split and not args.zero_inputs and not args.shape:
+        line["vs_frozen"] = round(value / frozen, 4)
+        if value < 0.95 * frozen:
+            print(f"[bench] WARNING: {w.name} at {value:.1f} TFLOP/s is more than 5% below its "
+                  f"frozen {frozen} TFLOP/s", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a row sample)", file=sys.stderr, flush=True)
         base, parity = cpu_baseline(x, w, o, lse, args.cpu_seconds)
@@ -372,7 +406,9 @@ def cpu_baseline_bwd(x, dout, w, grads_gpu, target_heads: int):
         e = a - r
         parity[name] = {"rms_rel": float(np.linalg.norm(e) / np.linalg.norm(r)),
                         "max_rel": float(np.abs(e).max() / np.abs(r).max())}
-    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    model, nproc = host_cpu()
+    base = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "cpu_model": model, "nproc": nproc, "kind": "oracle",
             "sample": f"{nh} of {w.B * w.H} heads of {w.short()}, every query and key of "
                       f"each (10 N^2 d flops per head); fp64 C oracle, {dt:.1f} s"}
     return base, parity
@@ -428,7 +464,7 @@ def bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev):
         + (" [all-zero inputs: power diagnostic]" if args.zero_inputs else ""),
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic, all zeros" if args.zero_inputs else "synthetic",
         "config": {"workload": f"{w.name}: attention backward (dQ, dK, dV from O, LSE, dO), "
                                f"{w.short()}, scale 1/sqrt({w.d})",

@@ -34,32 +34,72 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(report: bool = False, verbose: bool = False) -> str:
-    objs = []
-    build_dir = os.path.join(PKG, "_build")
+def _compile_cmd(src: str, obj: str, report: bool) -> list:
+    cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+           "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS,
+           *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    if report:
+        cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
+    return cmd
+
+
+def _compile_all(build_dir: str, report: bool, echo: bool) -> tuple:
+    """Compile every source into build_dir, in parallel; returns (objects, compiler text)."""
     os.makedirs(build_dir, exist_ok=True)
+    procs, objs = [], []
     for src in SOURCES:
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-               "-Wall", "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC, *DEVICE_FLAGS,
-               *FILE_FLAGS.get(src, []), "-c",
-               os.path.join(CSRC, src), "-o", obj]
-        if report:
-            cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        text = "\n".join(line for line in (res.stdout + res.stderr).splitlines()
-                         if "packed-fp32-ops" not in line)
-        if res.returncode != 0:
+        procs.append((src, subprocess.Popen(_compile_cmd(src, obj, report), stdout=subprocess.PIPE,
+                                            stderr=subprocess.STDOUT, text=True)))
+        objs.append(obj)
+    texts = []
+    for src, p in procs:
+        out = p.communicate()[0]
+        text = "\n".join(line for line in out.splitlines() if "packed-fp32-ops" not in line)
+        if p.returncode != 0:
             sys.stderr.write(text + "\n")
             raise RuntimeError(f"hipcc failed on {src}")
-        if report or verbose:
+        if echo:
             sys.stdout.write(text + "\n")
-        objs.append(obj)
+        texts.append(text)
+    return objs, "\n".join(texts)
+
+
+def build(report: bool = False, verbose: bool = False) -> str:
+    objs, _ = _compile_all(os.path.join(PKG, "_build"), report, report or verbose)
     tmp = LIB + ".tmp"
     subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
                    check=True)
     os.replace(tmp, LIB)
     return LIB
+
+
+def resource_usage(build_dir: str) -> dict:
+    """Compile every source into build_dir (the library itself is not touched) and return
+    the compiler's per-kernel resource record: {kernel: {"vgpr", "agpr", "scratch",
+    "vgpr_spill", "sgpr_spill", "occupancy"}} (scratch in bytes per lane)."""
+    _, text = _compile_all(build_dir, report=True, echo=False)
+    keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch",
+            "VGPRs Spill": "vgpr_spill", "SGPRs Spill": "sgpr_spill",
+            "Occupancy [waves/SIMD]": "occupancy"}
+    out, cur = {}, None
+    for line in text.splitlines():
+        if "remark:" not in line:
+            continue
+        body = line.split("remark:", 1)[1].split("[-Rpass")[0].strip()
+        if body.startswith("Function Name:"):
+            cur = body.split(":", 1)[1].strip()
+            out[cur] = {}
+            continue
+        if cur is None or ":" not in body:
+            continue
+        k, v = body.rsplit(":", 1)
+        if k.strip() in keys:
+            try:
+                out[cur][keys[k.strip()]] = int(v.strip())
+            except ValueError:
+                pass
+    return out
 
 
 if __name__ == "__main__":
