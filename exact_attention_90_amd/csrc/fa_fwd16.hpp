@@ -272,16 +272,18 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   //     overwritten, the row sum, l = alpha l + sum, and O = alpha O
   // The row sum adds the 32 values of P in score order, as a single pass would.
   //
-  // Where the output accumulators live in the matrix-core (AGPR) registers (d = 256, and
-  // two query blocks per wave), a multiply costs a read, the multiply and a write per
-  // element.  There the reference max mc moves only when a tile's row max exceeds it by
-  // more than kTau (base-2 units): P <= 2^kTau stays far inside binary16 range, softmax
-  // is unchanged by the choice of reference, and most tiles leave every alpha at 1, so O
-  // is rescaled in a wave-uniform branch that is rarely taken.  P > 1 then carries the
-  // binary16 rounding of values that are not powers of two even for the row's largest
-  // score, so O is normalised by the sum of P as rounded for the P V product (the
-  // weights applied to V sum to one) and LSE by the exact sum.
-  constexpr bool LAZY = D == 256 || RB == 2;
+  // At d >= 128 (LAZY) the reference max mc moves only when a tile's row max exceeds it
+  // by more than kTau (base-2 units): P <= 2^kTau stays far inside binary16 range,
+  // softmax is unchanged by the choice of reference, and most tiles leave every alpha at
+  // 1, so O is rescaled in a wave-uniform branch that is rarely taken instead of on every
+  // tile.  That matters most where the output accumulators live in the matrix-core
+  // (AGPR) registers (d = 256, two query blocks per wave), where a multiply costs a read,
+  // the multiply and a write per element; at d = 128 it saves 64 multiplies per tile
+  // (+1.5 % measured).  P > 1 then carries the binary16 rounding of values that are not
+  // powers of two even for the row's largest score, so O is normalised by the sum of P
+  // as rounded for the P V product (the weights applied to V sum to one) and LSE by the
+  // exact sum.  At d = 64 the rescale every tile measured faster.
+  constexpr bool LAZY = D >= 128;
   constexpr float kTau = RB == 2 ? 15.0f : 8.0f;
   constexpr int KC = C::KC;
   constexpr int NMX = NB >= 16 ? 2 : 1;  // B steps of the row max
@@ -578,12 +580,11 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
         pv_step(i, vf[i % DV], r);
         if (r == RB - 1 && i + DV < NB) vf[i % DV] = v_op(vb, i + DV);
         soft_b(i, r);
-        if constexpr (RB == 2) {
-          // chunk c: read at step 4c + 1, widened and written back at step 4c + 3
+        {
+          // chunk c: read at step (NB / CPT) c + 1, widened and written back at the
+          // chunk's last step
           if (r == 0 && i % (NB / CPT) == 1) widen_read(vw, i / (NB / CPT));
-          if (r == 1 && i % (NB / CPT) == NB / CPT - 1) widen_write(vw, i / (NB / CPT));
-        } else if (i % (NB / CPT) == NB / CPT - 1) {
-          widen_v(vw, i / (NB / CPT));
+          if (r == RB - 1 && i % (NB / CPT) == NB / CPT - 1) widen_write(vw, i / (NB / CPT));
         }
         __builtin_amdgcn_sched_barrier(0);
       }

@@ -109,8 +109,8 @@ int fa_fwd(const void *q, const void *k, const void *v, float *o, float *lse, in
  *           16-byte aligned (else FA_ERR_WORKSPACE): for row r = (b H + h) N + i and
  *           block t = 0 .. ceil(N/64) - 1, stats[(r ceil(N/64) + t) 2 + 0] is the kernel's
  *           running reference in base-2 units, log2(e) times the scaled score max over
- *           keys 0 .. 64 t + 63 (at d = 256 for 16-bit inputs a lagging reference at most
- *           8 below it, see the kernel), and stats[... + 1] the running sum of
+ *           keys 0 .. 64 t + 63 (at d >= 128 for 16-bit inputs a lagging reference at
+ *           most 8 below it, see the kernel), and stats[... + 1] the running sum of
  *           exp2(log2(e) s_j - reference) over those keys.
  * Returns FA_OK or an fa_status error code (as fa_fwd, plus FA_ERR_WORKSPACE).
  */

@@ -11,7 +11,7 @@ Tolerances are bounds derived from the arithmetic, per row and block (u = 2^-24)
   * the running sum is a float32 sum of n <= N terms exp2(fma(s_j, c, -ref)): each term's
     relative error is at most |d(s_j - m)| + ln2 u (|c s_j| + |ref|) + 2 u (the
     hardware exp2 is within one ulp), and the summation adds n u.
-For 16-bit inputs at d = 256 the kernel keeps a lagging reference (at most 8 base-2
+For 16-bit inputs at d >= 128 the kernel keeps a lagging reference (at most 8 base-2
 units below the max), so there the running log-sum ref ln2 + ln l is compared with
 m + ln l, and the reference is checked to lie within [m - 8 ln 2, m]."""
 import math
@@ -49,7 +49,7 @@ def test_block_statistics_match_the_recurrences(d, dtype):
     st = st.cpu().numpy().astype(np.float64)
     nb = (N + 63) // 64
     assert st.shape == (B, H, N, nb, 2)
-    lagging = dtype != "f32" and d == 256
+    lagging = dtype != "f32" and d >= 128
     qf, kf = (to_float32(x[n], dtype).astype(np.float64) for n in "qk")
     for b in range(B):
         for h in range(H):
