@@ -244,19 +244,26 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
   auto st_off = [&](int i) { return (C::KFLIP && (i & 1)) ? st_off1 : st_off0; };
   constexpr int ST_STEP = C::NT * 16;
   const int dma_wave = wu * 1024;
-  auto load_tile = [&](int stage, int qt) {
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      buf_load16_lds(qrs, Qs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
-                     qt * C::TILEB + i * ST_STEP);
-      buf_load16_lds(grs, Gs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
-                     qt * C::TILEB + i * ST_STEP);
-    }
+  auto load_chunk = [&](int stage, int qt, int i) {
+    buf_load16_lds(qrs, Qs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
+                   qt * C::TILEB + i * ST_STEP);
+    buf_load16_lds(grs, Gs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
+                   qt * C::TILEB + i * ST_STEP);
+  };
+  auto load_stats = [&](int stage, int qt) {
     // the tile's 64 values of lse2 and D (lanes 16..63 bring bytes no one reads)
     if (wu == 0) buf_load16_lds(lrs, Ls + stage * C::STATB, lane * 16, qt * 256);
     if (WANT_DK && wu == WAVES - 1)
       buf_load16_lds(drs, Ds + stage * C::STATB, lane * 16, qt * 256);
   };
+  auto load_tile = [&](int stage, int qt) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) load_chunk(stage, qt, i);
+    load_stats(stage, qt);
+  };
+  // at d >= 128 the next tile's loads ride one per step between the A0 matrix-core steps
+  // instead of all issuing before them
+  static_assert(D < 128 || CPT < C::KC, "one load per A0 step");
 
   f32x16 dk[WANT_DK ? OB : 1], dv[WANT_DV ? OB : 1];
 #pragma unroll
@@ -290,7 +297,8 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
   for (int qt = 0; qt < nqt; ++qt) {  // qt counts the range's tiles
     const int st = qt & 1;
     // the other stage held tile qt - 1, released by the barrier that ended it
-    if (qt + 1 < nqt) load_tile(st ^ 1, qt0 + qt + 1);
+    const bool more = qt + 1 < nqt;
+    if (D < 128 && more) load_tile(st ^ 1, qt0 + qt + 1);
     // held in registers across the loop rather than recomputed at each read
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) pin(a_off[kc]);
@@ -398,6 +406,8 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
           a_step(0, kc);
           if (kc + PA < KC) a_load(0, kc + PA);
           else a_load(1, kc + PA - KC);
+          if (more && kc < CPT) load_chunk(st ^ 1, qt0 + qt + 1, kc);
+          if (more && kc == CPT) load_stats(st ^ 1, qt0 + qt + 1);
           __builtin_amdgcn_sched_barrier(0);
         }
         stat_load(1);
@@ -561,15 +571,18 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
   auto st_off = [&](int i) { return (C::KFLIP && (i & 1)) ? st_off1 : st_off0; };
   constexpr int ST_STEP = C::NT * 16;
   const int dma_wave = wu * 1024;
+  auto load_chunk = [&](int stage, int kt, int i) {
+    buf_load16_lds(krs, Ks + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
+                   kt * C::TILEB + i * ST_STEP);
+    buf_load16_lds(vrs, Vs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
+                   kt * C::TILEB + i * ST_STEP);
+  };
   auto load_tile = [&](int stage, int kt) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      buf_load16_lds(krs, Ks + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
-                     kt * C::TILEB + i * ST_STEP);
-      buf_load16_lds(vrs, Vs + stage * C::TILEB + dma_wave + i * ST_STEP, st_off(i),
-                     kt * C::TILEB + i * ST_STEP);
-    }
+    for (int i = 0; i < CPT; ++i) load_chunk(stage, kt, i);
   };
+  // the next tile's loads ride one per k-step of the first block's S product
+  static_assert(CPT <= C::KC, "one load per k-step");
 
   f32x16 dq[OB];
 #pragma unroll
@@ -582,7 +595,7 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
   lds_barrier();
   for (int kt = 0; kt < nkt; ++kt) {  // kt counts the range's tiles
     const int st = kt & 1;
-    if (kt + 1 < nkt) load_tile(st ^ 1, kt0 + kt + 1);
+    const bool more = kt + 1 < nkt;
     const int kb = st * C::TILEB;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {  // 32-key blocks of the tile
@@ -595,6 +608,7 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
         const int off = kb + tl.rb + 32 * t * C::ROWB + ((32 * kc) ^ tl.rx);
         s = mma16<BF16>(lds_read16(Ks, off), qf[kc], s);
         dp = mma16<BF16>(lds_read16(Vs, off), gf[kc], dp);
+        if (t == 0 && more && kc < CPT) load_chunk(st ^ 1, kt0 + kt + 1, kc);
       }
       float ds[16];
 #pragma unroll
