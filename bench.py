@@ -56,16 +56,27 @@ FROZEN_TFLOPS = {"c3": 960.4, "c2": 809.0, "c4": 840.0, "c5": 1043.0, "d256": 81
 
 
 def host_cpu():
-    """The host CPU's model name (lscpu's 'Model name', from /proc/cpuinfo) and the number
-    of processors this process may run on."""
+    """The host CPU's model name (lscpu's 'Model name', else /proc/cpuinfo's) and the
+    number of processors this process may run on."""
+    import subprocess
+
     model = "unknown"
     try:
-        for line in open("/proc/cpuinfo"):
-            if line.lower().startswith("model name"):
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.strip().lower().startswith("model name"):
                 model = line.split(":", 1)[1].strip()
                 break
-    except OSError:
+    except (OSError, subprocess.SubprocessError):
         pass
+    if model == "unknown":
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
     try:
         nproc = len(os.sched_getaffinity(0))
     except AttributeError:

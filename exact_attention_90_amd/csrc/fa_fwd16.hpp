@@ -95,6 +95,10 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   constexpr int SB = C::SB, OB = C::OB, PU = C::PU, CPT = C::CPT;
   constexpr int NA = SB * C::KC;  // matrix-core steps of S^T = K Q^T per tile
   constexpr int NB = OB * PU;     // matrix-core steps of O^T += V^T P^T per tile
+  // every chunk of the next tiles' loads gets an S step of its own, and each chunk's
+  // widening a read step before its write step
+  static_assert(NA >= 2 * CPT, "the A half issues 2 CPT load chunks, one per step");
+  static_assert(NB % CPT == 0 && NB / CPT >= 2, "widening: read and write steps per chunk");
   constexpr int DK = 4;           // K operand reads kept in flight
   constexpr int DV = 3;           // V operand reads (pairs) kept in flight
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -189,16 +193,15 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
     for (int i = 0; i < CPT; ++i)
       buf_load16_lds(vrs, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB + i * ST_STEP);
   };
-  // one chunk of a tile's load.  SPREAD_LOADS: an iteration's loads ride one per step
-  // between its first matrix-core steps instead of all issuing before them (measured:
-  // bitwise the same results, +2.7 % at bf16 8x32x4096x128, +3.9 % at d = 256)
+  // one chunk of a tile's load: an iteration's loads ride one per step between its
+  // first matrix-core steps instead of all issuing before them (measured: bitwise the
+  // same results, +2.7 % at bf16 8x32x4096x128, +3.9 % at d = 256)
   auto dma_k1 = [&](char *kb, int kt, int i) __attribute__((always_inline)) {
     buf_load16_lds(krs, kb + dma_wave + i * ST_STEP, st_ki(i), kt * C::TILEB + i * ST_STEP);
   };
   auto dma_v1 = [&](char *vb, int kt, int i) __attribute__((always_inline)) {
     buf_load16_lds(vrs, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB + i * ST_STEP);
   };
-  constexpr bool SPREAD_LOADS = true;
   // bfloat16 V: the P V product runs in binary16, so each thread widens the chunks its
   // own loads wrote (chunk i: 16 bytes at dma_wave + i ST_STEP + 16 lane), in place.
   // Needs only this wave's loads to have landed; other waves read the stage after the
@@ -539,10 +542,6 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
 
     // ---- A ----
     st_tile = j;
-    if constexpr (!SPREAD_LOADS) {
-      dma_v(vw, j + 1);
-      dma_k(kw, j + 2);
-    }
     rescale_lazy();
 #pragma unroll
     for (int i = 0; i < DK; ++i) kf[i] = k_op(kb, i);
@@ -553,11 +552,9 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
       for (int r = 0; r < RB; ++r) {
         s_step(i, kf[i % DK], r);
         if (r == RB - 1 && i + DK < NA) kf[i % DK] = k_op(kb, i + DK);
-        if constexpr (SPREAD_LOADS) {
-          // V_{j+1} first (B waits for it alone), then K_{j+2}
-          if (r == 0 && i < CPT) dma_v1(vw, j + 1, i);
-          if (r == 0 && i >= CPT && i < 2 * CPT) dma_k1(kw, j + 2, i - CPT);
-        }
+        // V_{j+1} first (B waits for it alone), then K_{j+2}
+        if (r == 0 && i < CPT) dma_v1(vw, j + 1, i);
+        if (r == 0 && i >= CPT && i < 2 * CPT) dma_k1(kw, j + 2, i - CPT);
         // the last tile's keys past N are masked before its early max reads key block 0
         if (EARLY_MAX && MASKED && i == KC + 1 && r == 0 && nlast < C::BN)
           mask_block(0, nlast);
