@@ -22,9 +22,12 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of every device code object.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-file code-generation choices: the d = 128 forward kernel takes its S products in
-# vector-register form (its P V products accumulate in AGPRs through assembly).
-FILE_FLAGS = {"fa_fwd16_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# Per-file code-generation choices: the 16-bit forward kernels take the compiler's own
+# matrix-core products (S) in vector-register form; where O does not fit beside them
+# (d = 256) the P V products accumulate in AGPRs through their own assembly.  (The d = 64
+# kernels compile to the same code either way.)
+FILE_FLAGS = {"fa_fwd16_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "fa_fwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

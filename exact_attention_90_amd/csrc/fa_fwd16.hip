@@ -2,7 +2,10 @@
 // dispatch over head sizes (d = 128 is compiled in fa_fwd16_d128.hip).  Both use four
 // 32-row waves per workgroup: at d = 64 the softmax dominates and three waves per SIMD
 // schedule best; at d = 256 one 32-row wave already needs more than half of a SIMD's
-// registers.
+// registers.  Compiled with the compiler's own products in vector-register form: at
+// d = 256 O sits in AGPRs (its products written as assembly) and S in VGPRs, so S is
+// never copied out of AGPRs (+2 % against S in AGPRs, bitwise the same output); the
+// d = 64 code does not change.
 #include "fa_fwd16.hpp"
 
 namespace fa {

@@ -306,6 +306,11 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // row max over key block 0 (complete after A step KC - 1) is taken there, on A steps
   // KC + 2 .. 2 KC - 1 (EARLY_MAX), and B takes only key block 1's.
   constexpr bool EARLY_MAX = RB == 2;
+  // The P V products go through their own assembly into AGPR accumulators whenever O
+  // cannot share the vector registers with S: two query blocks per wave, or d = 256 (O
+  // alone is 128 registers).  The unit is then compiled with the compiler's own
+  // products (S) in vector-register form, so S is never copied out of AGPRs.
+  constexpr bool ASMPV = RB == 2 || D == 256;
   constexpr int NAM = KC - 2;  // A steps carrying the key-block-0 max
   auto max_range = [&](int b, int e, int r) __attribute__((always_inline)) {
     if (b == 0) mx[r] = s[r][0][0];
@@ -451,7 +456,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // fresh definitions there, so that every later read of the accumulators (the lazy
   // rescale, copies the compiler makes, the epilogue) follows the wait
   auto settle_o = [&]() __attribute__((always_inline)) {
-    if constexpr (RB == 2) {
+    if constexpr (ASMPV) {
       mfma_drain();
 #pragma unroll
       for (int r = 0; r < RB; ++r)
@@ -463,7 +468,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // P V product step i of block r: one V operand feeds every query block of the wave
   auto pv_step = [&](int i, u32x4 vop, int r) __attribute__((always_inline)) {
     const int u = i / OB, e = i % OB;
-    if constexpr (RB == 2)
+    if constexpr (ASMPV)
       asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
                    : "+a"(o[r][e])
                    : "v"(vop), "v"(pf[r][u]));
@@ -602,7 +607,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
     for (int k = 0; k < NA; ++k)
 #pragma unroll
       for (int r = 0; r < RB; ++r) soft_a(k, r, false);
-    if constexpr (RB == 2) mfma_drain();
+    if constexpr (ASMPV) mfma_drain();
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const u32x4 vop = v_op(vb, i);
