@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import statistics
 import json
 import math
 import os
@@ -375,7 +376,9 @@ def main() -> int:
             "traffic": traffic,
             "kernel": "fa_fwd16_kernel" if w.dtype != "f32" else "fa_fwd32_kernel",
             "avg_launch_ms": round(avg_launch_ms, 5),
+            "median_launch_ms": round(statistics.median(per), 5),
             "min_launch_ms": round(min(per), 5),
+            "tflops_at_median": round(flops / (statistics.median(per) * 1e-3) / 1e12, 3),
             "kernel_src": kernel_source_hash(),
         },
         "cpu_baseline": None,
@@ -487,7 +490,10 @@ def bench_bwd(args, w, x, q, k, v, o, lse, scale32, dev):
                      "frac": round(flops / (avg * 1e-3) / 1e12 / peak, 4),
                      "traffic": rec.get("bytes_per_launch") if rec else None,
                      "kernel": "fa_bwd (prep + dkdv + dq kernels)",
-                     "avg_launch_ms": round(avg, 5), "min_launch_ms": round(min(per), 5),
+                     "avg_launch_ms": round(avg, 5),
+                     "median_launch_ms": round(statistics.median(per), 5),
+                     "min_launch_ms": round(min(per), 5),
+                     "tflops_at_median": round(flops / (statistics.median(per) * 1e-3) / 1e12, 3),
                      "kernel_src": kernel_source_hash(BWD_KERNEL_SOURCES)},
         "cpu_baseline": None,
     }
