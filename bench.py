@@ -46,6 +46,8 @@ KERNEL_SOURCES = ("exact_attention_90_amd/csrc/fa_fused.hip",
 # the backward kernels have their own hash (bench --pass bwd), so that a change to them
 # does not invalidate the forward pass's committed counters
 BWD_KERNEL_SOURCES = ("exact_attention_90_amd/csrc/fa_bwd.hip",
+                      "exact_attention_90_amd/csrc/fa_bwd.hpp",
+                      "exact_attention_90_amd/csrc/fa_bwd_d128.hip",
                       "exact_attention_90_amd/csrc/fa_softmax.hpp",
                       "exact_attention_90_amd/csrc/fa_device.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.md")

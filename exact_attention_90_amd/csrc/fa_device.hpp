@@ -55,6 +55,16 @@ __device__ __forceinline__ f32x16 mma_f32(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// Matrix-core products written as assembly (accumulating in AGPRs) are not tracked by
+// the compiler's hazard recognizer: vector code that reads their accumulators must first
+// wait for the last product explicitly.  24 wait states, more than the 19 of the longest
+// (16-pass) product; the fences keep the wait where it is placed.
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // ---- lane exchange --------------------------------------------------------------
 // v_permlane32_swap(a, b) swaps the upper 32 lanes of a with the lower 32 lanes of b.
 // With a = b = x the two results hold, on every lane l, x[min(l, l^32)] and

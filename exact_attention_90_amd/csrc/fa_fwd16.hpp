@@ -65,18 +65,12 @@ struct Cfg16 {
   static_assert(RSTEP % 8 == 0, "thread row stride must keep the swizzle keys periodic");
 };
 
-// With two query blocks per wave the P V products are written as assembly that
-// accumulates in the matrix-core (AGPR) registers, and the compiler does not track the
-// latency of assembly: vector code that reads those accumulators first waits for the
-// last product explicitly (more than the 19 wait states of the longest, 16-pass,
-// product), and the packed P operands are written at least one whole matrix-core step
-// before a product reads them (scheduling fences separate the pipeline steps; after the
-// last tile's softmax this wait separates them).
-__device__ __forceinline__ void mfma_drain() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
+// With two query blocks per wave, or at d = 256, the P V products are written as
+// assembly that accumulates in the matrix-core (AGPR) registers (mfma_drain, in
+// fa_device.hpp, covers the latency the compiler does not track), and the packed P
+// operands are written at least one whole matrix-core step before a product reads them
+// (scheduling fences separate the pipeline steps; after the last tile's softmax a drain
+// separates them).
 
 // RB = 32-row query blocks per wave.  With RB = 2 every K operand read from LDS feeds
 // the S products of both blocks and every V operand read feeds both P V products, which
