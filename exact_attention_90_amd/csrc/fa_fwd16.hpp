@@ -53,8 +53,9 @@ struct Cfg16 {
   static constexpr int LDS = 4 * TILEB;         // K and V, two stages each
   // minimum waves per SIMD the registers must allow: at d = 256 one 32-row wave holds
   // O (128 registers) and Q (64), and a wave of two 32-row blocks at d = 128 holds two
-  // of each; both need more than half of the register file
-  static constexpr int WPE = (D == 256 || RB == 2) ? 1 : 8 / WAVES;
+  // of each; both need more than half of the register file.  Two 32-row blocks at d = 64
+  // (O 64, Q 32, S 64, P 32) fit two waves per SIMD.
+  static constexpr int WPE = (D == 256 || (RB == 2 && D > 64)) ? 1 : RB == 2 ? 2 : 8 / WAVES;
   static_assert(CPT >= 1 && TILEB % (16 * NT) == 0, "a tile is whole chunks per thread");
   static_assert(BM * ROWB <= LDS, "Q staging must fit in the K and V stages");
   // the rows a thread moves differ by RSTEP per chunk.  The V swizzle key (period 4
@@ -93,8 +94,10 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // widening a read step before its write step
   static_assert(NA >= 2 * CPT, "the A half issues 2 CPT load chunks, one per step");
   static_assert(NB % CPT == 0 && NB / CPT >= 2, "widening: read and write steps per chunk");
-  constexpr int DK = 4;           // K operand reads kept in flight
-  constexpr int DV = 3;           // V operand reads (pairs) kept in flight
+  // K operand reads and V operand read pairs kept in flight (fewer for two blocks at
+  // d = 64, which must fit two waves per SIMD)
+  constexpr int DK = (D == 64 && RB == 2) ? 3 : 4;
+  constexpr int DV = (D == 64 && RB == 2) ? 2 : 3;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *const Ks = smem;
   char *const Vs = smem + 2 * C::TILEB;
@@ -301,10 +304,12 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // KC + 2 .. 2 KC - 1 (EARLY_MAX), and B takes only key block 1's.
   constexpr bool EARLY_MAX = RB == 2;
   // The P V products go through their own assembly into AGPR accumulators whenever O
-  // cannot share the vector registers with S: two query blocks per wave, or d = 256 (O
-  // alone is 128 registers).  The unit is then compiled with the compiler's own
-  // products (S) in vector-register form, so S is never copied out of AGPRs.
-  constexpr bool ASMPV = RB == 2 || D == 256;
+  // cannot share the vector registers with S: two query blocks per wave at d = 128, or
+  // d = 256 (O alone is 128 registers).  The unit is then compiled with the compiler's
+  // own products (S) in vector-register form, so S is never copied out of AGPRs.  (Two
+  // blocks at d = 64 keep everything in vector registers: 255-256 of them, two waves
+  // per SIMD.)
+  constexpr bool ASMPV = (RB == 2 && D > 64) || D == 256;
   constexpr int NAM = KC - 2;  // A steps carrying the key-block-0 max
   auto max_range = [&](int b, int e, int r) __attribute__((always_inline)) {
     if (b == 0) mx[r] = s[r][0][0];

@@ -24,7 +24,7 @@ KNOWN_SCRATCH = {
 # (kernel name pattern, waves per SIMD) of the production 16-bit forward kernels
 OCCUPANCY = [
     (r"fa_fwd16_kernelILi128ELb[01]ELi8ELi1ELb0E", 2),
-    (r"fa_fwd16_kernelILi64ELb[01]ELi4ELi1ELb0E", 3),
+    (r"fa_fwd16_kernelILi64ELb[01]ELi4ELi2ELb0E", 2),
     (r"fa_fwd16_kernelILi256ELb[01]ELi4ELi1ELb0E", 1),
 ]
 
