@@ -71,17 +71,19 @@ def test_tiny_and_ragged(N, dtype, d):
 # tiles of both workgroup sizes: every length of the software-pipelined loop, with the
 # masked iteration alone (2 tiles) and after odd and even numbers of steady iterations
 @pytest.mark.parametrize("N", [65, 191, 257, 449, 640])
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64), ("bf16", 64)])
 def test_pipeline_lengths(N, dtype, d):
     m, _, _ = full_case(1, 2, N, d, dtype, seed=300 + N)
     assert_parity(m, dtype, where=f"N={N} d={d} {dtype}")
 
 
-@pytest.mark.parametrize("dtype,mult", [("bf16", 3.0), ("f16", 8.0), ("bf16", 12.0)])
-def test_large_logits(dtype, mult):
+@pytest.mark.parametrize("dtype,mult,d", [("bf16", 3.0, 128), ("f16", 8.0, 128), ("bf16", 12.0, 128),
+                                          ("f16", 8.0, 64), ("bf16", 12.0, 64)])
+def test_large_logits(dtype, mult, d):
     # logit standard deviation ~ mult^2: needs the running-max subtraction and rescale
-    m, _, _ = full_case(1, 2, 2000, 128, dtype, seed=77, mult=mult)
-    assert_parity(m, dtype, where=f"x{mult}")
+    # (at d = 64 with the row max of each wave's two query blocks taken in different steps)
+    m, _, _ = full_case(1, 2, 2000, d, dtype, seed=77, mult=mult)
+    assert_parity(m, dtype, where=f"x{mult} d={d}")
 
 
 def test_empty_problem():
