@@ -88,10 +88,15 @@ def host_cpu():
 
 
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
+    """Hash of the kernels' code: the sources with line comments, indentation and blank
+    lines removed, so that a comment edit keeps the committed counter records valid."""
     h = hashlib.sha256()
     for rel in sources:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            for line in f:
+                code = re.sub(r"//.*$", "", line).strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

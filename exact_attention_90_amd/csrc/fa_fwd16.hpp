@@ -75,8 +75,9 @@ struct Cfg16 {
 
 // RB = 32-row query blocks per wave.  With RB = 2 every K operand read from LDS feeds
 // the S products of both blocks and every V operand read feeds both P V products, which
-// halves the LDS operand bytes per flop; the two blocks' output accumulators then need
-// the matrix-core (AGPR) registers, and one wave runs per SIMD.
+// halves the LDS operand bytes per flop.  At d = 64 the two blocks fit two waves per SIMD
+// in vector registers; at d = 128 their output accumulators need the matrix-core (AGPR)
+// registers, and one wave runs per SIMD.
 //
 // STATS: the statistics-recording form (validation only, nsplit = 1): after every key
 // tile t each query row's running max (base-2 units, c m) and row sum go to
@@ -277,9 +278,9 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // softmax is unchanged by the choice of reference, and most tiles leave every alpha at
   // 1, so O is rescaled in a wave-uniform branch that is rarely taken instead of on every
   // tile.  That matters most where the output accumulators live in the matrix-core
-  // (AGPR) registers (d = 256, two query blocks per wave), where a multiply costs a read,
-  // the multiply and a write per element; at d = 128 it saves 64 multiplies per tile
-  // (+1.5 % measured).  P > 1 then carries the binary16 rounding of values that are not
+  // (AGPR) registers (d = 256, two query blocks per wave at d = 128), where a multiply
+  // costs a read, the multiply and a write per element; at d = 128 it saves 64
+  // multiplies per tile (+1.5 % measured).  P > 1 then carries the binary16 rounding of values that are not
   // powers of two even for the row's largest score, so O is normalised by the sum of P
   // as rounded for the P V product (the weights applied to V sum to one) and LSE by the
   // exact sum.  At d = 64 the rescale every tile measured faster.
