@@ -48,6 +48,7 @@ KERNEL_SOURCES = ("exact_attention_90_amd/csrc/fa_fused.hip",
 BWD_KERNEL_SOURCES = ("exact_attention_90_amd/csrc/fa_bwd.hip",
                       "exact_attention_90_amd/csrc/fa_bwd.hpp",
                       "exact_attention_90_amd/csrc/fa_bwd_d128.hip",
+                      "exact_attention_90_amd/csrc/fa_bwd_d256.hip",
                       "exact_attention_90_amd/csrc/fa_softmax.hpp",
                       "exact_attention_90_amd/csrc/fa_device.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.md")

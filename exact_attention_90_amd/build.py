@@ -17,19 +17,21 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 SOURCES = ["fa_api.cpp", "fa_fused.hip", "fa_fwd16.hip", "fa_fwd16_d128.hip", "fa_naive.hip",
-           "fa_bwd.hip", "fa_bwd_d128.hip", "fa_bwd32.hip"]
+           "fa_bwd.hip", "fa_bwd_d128.hip", "fa_bwd_d256.hip", "fa_bwd32.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are kept out of every device code object.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-file code-generation choices: the 16-bit forward kernels and the d = 128 backward
-# kernels take the compiler's own matrix-core products (S, dP) in vector-register form;
+# Per-file code-generation choices: the 16-bit forward kernels and the d = 128 (and the
+# d = 256 dV and dQ) backward kernels take the compiler's own matrix-core products (S, dP)
+# in vector-register form;
 # where the accumulators do not fit beside them
 # (d = 256; the backward's dV and dK at d = 128) the accumulating products go to AGPRs
 # through their own assembly.  (The d = 64 kernels compile to the same code either way.)
 FILE_FLAGS = {"fa_fwd16_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
               "fa_fwd16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-              "fa_bwd_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "fa_bwd_d128.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "fa_bwd_d256.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

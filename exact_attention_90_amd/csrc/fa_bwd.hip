@@ -1,13 +1,25 @@
-// Launch of the 16-bit backward pass (kernels in fa_bwd.hpp; d = 128 is compiled in
-// fa_bwd_d128.hip) and of the split backward's slot sums.
+// Launch of the 16-bit backward pass (kernels in fa_bwd.hpp; d = 128, and the dV and dQ
+// launches of d = 256, are compiled in fa_bwd_d128.hip and fa_bwd_d256.hip) and of the
+// split backward's slot sums.
 #include "fa_bwd.hpp"
 
 namespace fa {
 
+// d = 256: prep and the dK-only key-owned launch here, the dV-only launch and dQ in
+// fa_bwd_d256.hip (compiled for S and dP in vector registers)
+template <bool BF16>
+static hipError_t run_bwd_d256(const BwdProblem &p, float *dq, float *dk, float *dv, int nsplit,
+                               int tps, hipStream_t stream) {
+  hipError_t e = run_bwd_prep<256, BF16>(p, stream);
+  if (e == hipSuccess) e = launch_bwd16_d256_dv_dq(p, dq, dv, nsplit, tps, stream);
+  if (e == hipSuccess) e = run_bwd_dkdv<256, BF16, kDK>(p, dk, nullptr, nsplit, tps, stream);
+  return e;
+}
+
 template <bool BF16>
 static hipError_t run_bwd_any(const BwdProblem &p, float *dq, float *dk, float *dv, int nsplit,
                               int tps, hipStream_t stream) {
-  return p.d == 256   ? run_bwd<256, BF16>(p, dq, dk, dv, nsplit, tps, stream)
+  return p.d == 256   ? run_bwd_d256<BF16>(p, dq, dk, dv, nsplit, tps, stream)
          : p.d == 128 ? launch_bwd16_d128(p, dq, dk, dv, nsplit, tps, stream)
                       : run_bwd<64, BF16>(p, dq, dk, dv, nsplit, tps, stream);
 }

@@ -227,11 +227,13 @@ __global__ __launch_bounds__(64 * WAVES, dkdv_wpe<D>()) void fa_bwd_dkdv_kernel(
   // the wave's 32 keys: K and V rows as B operands (lane: key l32, columns 8h.. of each
   // 16-column k-step); keys past N read zeros
   constexpr bool WANT_DK = (WHAT & kDK) != 0, WANT_DV = (WHAT & kDV) != 0;
-  // At d = 128 the dV and dK products are written as assembly accumulating in AGPRs, and
-  // the unit that instantiates this kernel (fa_bwd_d128.hip) is compiled with the
-  // compiler's own products (S, dP) in vector-register form: the S and dP values are
-  // then never copied out of AGPRs (128 moves per tile fewer, +5 %, bitwise the same).
-  constexpr bool ASM_DKDV = D == 128;
+  // At d = 128, and for the dV-only launch at d = 256, the dV and dK products are written
+  // as assembly accumulating in AGPRs, and the unit that instantiates the kernel
+  // (fa_bwd_d128.hip, fa_bwd_d256.hip) is compiled with the compiler's own products (S,
+  // dP) in vector-register form: S and dP are then never copied out of AGPRs (d = 128:
+  // 128 moves per tile fewer, +5 %; d = 256, dV: +9 %; bitwise the same).  The dK-only
+  // launch at d = 256 needs the AGPRs for S and dP (its vector registers are full).
+  constexpr bool ASM_DKDV = D == 128 || (D == 256 && !WANT_DK);
   const int key = k0 + 32 * w + l32;
   u32x4 kf[KC], vf[WANT_DK ? KC : 1];
 #pragma unroll
@@ -661,7 +663,29 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
           const int o0 = kb + tl.tb0 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
           const int o1 = kb + tl.tb1 + 16 * u * C::ROWB + ((64 * e) ^ tl.tx);
           const u32x2 a0 = lds_read_tr(Ks, o0), a1 = lds_read_tr(Ks, o1);
-          dq[e] = mma16<BF16>(u32x4{a0[0], a0[1], a1[0], a1[1]}, sf, dq[e]);
+          if constexpr (D == 256) {
+            // dQ accumulates in AGPRs through assembly (fa_bwd_d256.hip keeps S and dP in
+            // vector registers).  The first product of a key step reads dS packed just
+            // before it: at least two wait states after that vector write.
+            const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
+            if constexpr (BF16) {
+              if (e == 0)
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                             : "+a"(dq[e]) : "v"(av), "v"(sf));
+              else
+                asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                             : "+a"(dq[e]) : "v"(av), "v"(sf));
+            } else {
+              if (e == 0)
+                asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+                             : "+a"(dq[e]) : "v"(av), "v"(sf));
+              else
+                asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0"
+                             : "+a"(dq[e]) : "v"(av), "v"(sf));
+            }
+          } else {
+            dq[e] = mma16<BF16>(u32x4{a0[0], a0[1], a1[0], a1[1]}, sf, dq[e]);
+          }
         }
       }
     }
@@ -669,6 +693,13 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
     lds_barrier();
   }
 
+  if constexpr (D == 256) {
+    // the assembly products' results: wait for the last, then fresh definitions
+    mfma_drain();
+#pragma unroll
+    for (int e = 0; e < OB; ++e) asm volatile("" : "+a"(dq[e]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
   constexpr int WAVE_LDS = (C::LDS / WAVES) & ~15;
   const int row0 = q0 + 32 * w;
   store_rows_lds<D, 1, false>(dq, 0.f, 1.f, 0.5f / scale, smem + w * WAVE_LDS,
@@ -678,58 +709,65 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
 // ------------------------------------------------------------------------------------
 
 // nsplit ranges of tps streamed tiles each; dq, dk, dv receive nsplit slots of B H N d
-// floats (with nsplit = 1 they are the gradients themselves)
+// floats (with nsplit = 1 they are the gradients themselves).  The three steps are
+// separate functions so that a head size's kernels can be instantiated in the unit whose
+// code-generation choices suit them (fa_bwd_d128.hip, fa_bwd_d256.hip).
+template <int D, bool BF16>
+static hipError_t run_bwd_prep(const BwdProblem &p, hipStream_t stream) {
+  const int64_t rows = int64_t(p.B) * p.H * p.N;
+  const int64_t blocks = (rows * (D / 4) + 255) / 256;
+  const int grid = int(blocks < kMaxGrid ? blocks : kMaxGrid);
+  hipLaunchKernelGGL((fa_bwd_prep_kernel<D, BF16>), dim3(grid), dim3(256), 0, stream, p.o,
+                     p.dout, p.lse, static_cast<uint16_t *>(p.ws_do16), p.ws_lse2, p.ws_d, rows);
+  return hipGetLastError();
+}
+
+// dK and dV (WHAT = kDK | kDV), or one of them (d = 256: one launch for each)
+template <int D, bool BF16, int WHAT>
+static hipError_t run_bwd_dkdv(const BwdProblem &p, float *dk, float *dv, int nsplit, int tps,
+                               hipStream_t stream) {
+  constexpr int WAVES = 4;
+  using C = CfgB<D, WAVES>;
+  const int nb = (p.N + C::BR - 1) / C::BR;
+  const int G = nb * p.B * p.H * nsplit;
+  auto kern = fa_bwd_dkdv_kernel<D, BF16, WAVES, WHAT>;
+  const hipError_t ea = allow_lds_on_device<fa_bwd_dkdv_kernel<D, BF16, WAVES, WHAT>>(C::LDS);
+  if (ea != hipSuccess) return ea;
+  hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
+                     static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
+                     static_cast<const uint16_t *>(p.v),
+                     static_cast<const uint16_t *>(p.ws_do16), p.ws_lse2, p.ws_d, dk, dv,
+                     p.N, nb, G, p.scale * kLog2e, p.scale, nsplit, tps);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+static hipError_t run_bwd_dq(const BwdProblem &p, float *dq, int nsplit, int tps,
+                             hipStream_t stream) {
+  constexpr int WAVES = 4;
+  using C = CfgB<D, WAVES>;
+  const int nb = (p.N + C::BR - 1) / C::BR;
+  const int G = nb * p.B * p.H * nsplit;
+  auto kern = fa_bwd_dq_kernel<D, BF16, WAVES>;
+  const hipError_t ea = allow_lds_on_device<fa_bwd_dq_kernel<D, BF16, WAVES>>(C::LDS);
+  if (ea != hipSuccess) return ea;
+  hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
+                     static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
+                     static_cast<const uint16_t *>(p.v),
+                     static_cast<const uint16_t *>(p.ws_do16), p.ws_lse2, p.ws_d, dq, p.N,
+                     nb, G, p.scale * kLog2e, p.scale, nsplit, tps);
+  return hipGetLastError();
+}
+
+// the whole pass for d <= 128 (one key-owned launch for dK and dV)
 template <int D, bool BF16>
 static hipError_t run_bwd(const BwdProblem &p, float *dq, float *dk, float *dv, int nsplit,
                           int tps, hipStream_t stream) {
-  constexpr int WAVES = 4;
-  using C = CfgB<D, WAVES>;
-  const int64_t rows = int64_t(p.B) * p.H * p.N;
-  uint16_t *dO16 = static_cast<uint16_t *>(p.ws_do16);
-  // prep
-  {
-    const int64_t blocks = (rows * (D / 4) + 255) / 256;
-    const int grid = int(blocks < kMaxGrid ? blocks : kMaxGrid);
-    hipLaunchKernelGGL((fa_bwd_prep_kernel<D, BF16>), dim3(grid), dim3(256), 0, stream, p.o,
-                       p.dout, p.lse, dO16, p.ws_lse2, p.ws_d, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const float c = p.scale * kLog2e;
-  const int nb = (p.N + C::BR - 1) / C::BR;
-  const int G = nb * p.B * p.H * nsplit;
-  // dK and dV: one launch, or (d = 256) one for dV and one for dK
-  auto dkdv = [&](auto what) -> hipError_t {
-    auto kern = fa_bwd_dkdv_kernel<D, BF16, WAVES, decltype(what)::value>;
-    const hipError_t ea =
-        allow_lds_on_device<fa_bwd_dkdv_kernel<D, BF16, WAVES, decltype(what)::value>>(C::LDS);
-    if (ea != hipSuccess) return ea;
-    hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
-                       static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
-                       static_cast<const uint16_t *>(p.v), dO16, p.ws_lse2, p.ws_d, dk, dv,
-                       p.N, nb, G, c, p.scale, nsplit, tps);
-    return hipGetLastError();
-  };
-  {
-    hipError_t e;
-    if constexpr (D == 256) {
-      e = dkdv(std::integral_constant<int, kDV>{});
-      if (e == hipSuccess) e = dkdv(std::integral_constant<int, kDK>{});
-    } else {
-      e = dkdv(std::integral_constant<int, kDK | kDV>{});
-    }
-    if (e != hipSuccess) return e;
-  }
-  {
-    auto kern = fa_bwd_dq_kernel<D, BF16, WAVES>;
-    const hipError_t ea = allow_lds_on_device<fa_bwd_dq_kernel<D, BF16, WAVES>>(C::LDS);
-    if (ea != hipSuccess) return ea;
-    hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
-                       static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
-                       static_cast<const uint16_t *>(p.v), dO16, p.ws_lse2, p.ws_d, dq, p.N,
-                       nb, G, c, p.scale, nsplit, tps);
-  }
-  return hipGetLastError();
+  static_assert(D <= 128, "d = 256 runs its dV, dK and dQ launches from two units");
+  hipError_t e = run_bwd_prep<D, BF16>(p, stream);
+  if (e == hipSuccess) e = run_bwd_dkdv<D, BF16, kDK | kDV>(p, dk, dv, nsplit, tps, stream);
+  if (e == hipSuccess) e = run_bwd_dq<D, BF16>(p, dq, nsplit, tps, stream);
+  return e;
 }
 
 }  // namespace fa

@@ -81,6 +81,9 @@ hipError_t launch_bwd(const BwdProblem &p, hipStream_t stream);    // every dtyp
 // the 16-bit backward at d = 128 (fa_bwd_d128.hip): nsplit ranges of tps tiles each
 hipError_t launch_bwd16_d128(const BwdProblem &p, float *dq, float *dk, float *dv, int nsplit,
                              int tps, hipStream_t stream);
+// the dV-only and dQ launches of the 16-bit backward at d = 256 (fa_bwd_d256.hip)
+hipError_t launch_bwd16_d256_dv_dq(const BwdProblem &p, float *dq, float *dv, int nsplit,
+                                   int tps, hipStream_t stream);
 // nsplit ranges of tps tiles (64 rows) each; parts holds 3 nsplit slots of
 // B H N d floats (dQ slots, then dK, then dV), summed into p.dq, p.dk, p.dv
 hipError_t launch_bwd_split(const BwdProblem &p, float *parts, int nsplit, int tps,
