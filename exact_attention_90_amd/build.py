@@ -109,6 +109,20 @@ def resource_usage(build_dir: str) -> dict:
     return out
 
 
+def device_assembly(src: str, out_path: str) -> str:
+    """The gfx950 assembly of one source as the library builds it (same flags), written to
+    out_path; returns its text."""
+    cmd = [hipcc(), "-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-I", INCLUDE,
+           "-I", CSRC, *DEVICE_FLAGS, *FILE_FLAGS.get(src, []), "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", out_path]
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if p.returncode != 0:
+        sys.stderr.write(p.stdout)
+        raise RuntimeError(f"hipcc -S failed on {src}")
+    with open(out_path) as f:
+        return f.read()
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--report", action="store_true")

@@ -689,6 +689,10 @@ __global__ __launch_bounds__(64 * WAVES, dq_wpe<D>()) void fa_bwd_dq_kernel(
         }
       }
     }
+    // the assembly products' latency is waited out inside the loop: the register
+    // allocator may place copies of the accumulators at the loop's exit, ahead of any wait
+    // written after it
+    if constexpr (D == 256) mfma_drain();
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     lds_barrier();
   }
