@@ -5,7 +5,7 @@
 // (same guide, "FlashAttention-2 improvement") and the Q-resident, K/V-streaming
 // loop order of the pwwt.cn CK/MI50 notes (section 2.2).  Per workgroup:
 //
-//   prologue  Q tile [128 x d] -> LDS with coalesced 16-byte loads -> registers
+//   prologue  Q tile [BM x d] -> LDS with coalesced 16-byte loads -> registers
 //   loop      K_j, V_j tiles stream through two LDS stages; while tile j is used,
 //             tile j+1 is already in flight from global memory
 //             S^T = K_j Q^T on the matrix cores (fp32 accumulate)
@@ -16,8 +16,10 @@
 //             O^T += V_j^T P^T on the matrix cores
 //   epilogue  O / l and LSE = m*scale + ln l to global memory
 //
-// Layout of the work on the chip: 4 waves x 32 query rows.  Each wave computes S^T so
-// that every lane owns ONE query row and 16 (of 32) keys per 32x32 block: the row
+// This unit holds the fp32-input kernel, the merge of key ranges and the dispatch (the
+// 16-bit kernel is fa_fwd16.hpp).  Layout of the fp32 kernel's work on the chip: 4 waves
+// x 32 query rows.  Each wave computes S^T so that every lane owns ONE query row and 16
+// (of 32) keys per 32x32 block: the row
 // max and row sum are in-lane reductions plus one exchange with lane ^ 32, and the
 // rescale factor alpha is a per-lane scalar.  The P registers feed the P V product
 // directly; V stays row-major in LDS and its operand is fetched with the
