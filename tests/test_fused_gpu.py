@@ -86,6 +86,37 @@ def test_large_logits(dtype, mult, d):
     assert_parity(m, dtype, where=f"x{mult} d={d}")
 
 
+@pytest.mark.parametrize("scale", [1e-6, 50.0])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_extreme_scales(dtype, d, scale):
+    # scale 1e-6: every logit ~0, P ~1 everywhere (O is the column mean, LSE ~ ln N, the
+    # row sum over every key); scale 50: logit spread ~50 sqrt(d), one key per row
+    # dominates and the running max jumps by far more than the lagging reference's reach
+    m, x, _ = full_case(1, 2, 333, d, dtype, seed=900 + d, scale=scale)
+    tol = None
+    if dtype == "f32" and scale > 1.0:
+        # the 1e-5 bar assumes moderate logits.  Here each logit is an fp32 dot product
+        # with |ds_j| <= scale (d + 1) u sum_k |q_k k_jk| (u = 2^-24), ~1e-2 at scale 50,
+        # and to first order |dO| <= sum_j p_j (|ds_j| + sum_l p_l |ds_l|) |v_j - O|; that
+        # bound (worst-case signs) is the tolerance, and the direction of O must still
+        # agree to 1e-7 (a wrong rescale would not)
+        q, k, v = (to_float32(x[n], dtype).astype(np.float64) for n in "qkv")
+        sc = float(np.float32(scale))
+        s_ = sc * np.einsum("bhid,bhjd->bhij", q, k)
+        p_ = np.exp(s_ - s_.max(-1, keepdims=True))
+        p_ /= p_.sum(-1, keepdims=True)
+        o_ = np.einsum("bhij,bhjd->bhid", p_, v)
+        dl = sc * (d + 1) * 2.0**-24 * np.einsum("bhid,bhjd->bhij", np.abs(q), np.abs(k))
+        w_ = p_ * (dl + (p_ * dl).sum(-1, keepdims=True))
+        tol = 1e-5
+        for h in range(v.shape[1]):  # one head at a time: [N, N, d] per head
+            diff = np.abs(v[0, h][None, :, :] - o_[0, h][:, None, :])
+            tol = max(tol, float(np.einsum("ij,ijd->id", w_[0, h], diff).max()))
+        assert m["cosine"] >= 1.0 - 1e-7, m
+    assert_parity(m, dtype, max_abs=tol, where=f"scale={scale} d={d} {dtype}")
+
+
 def test_empty_problem():
     import torch
 
