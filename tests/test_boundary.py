@@ -85,6 +85,7 @@ def call(lib, q=A, k=B_, v=C_, o=O_, lse=L_, B=1, H=1, N=128, d=64, scale=0.125,
     (dict(B=2**20, H=2**10, N=2**12), 2),                    # grid beyond 2^24 workgroups
     (dict(B=2**16, H=2**16, N=1), 2),                        # B*H beyond int
     (dict(N=2**23, d=128, dtype=1), 2),                      # one head beyond 2^31 bytes
+    (dict(N=2**23 - 511, d=128, dtype=2), 2),                # one tile short of it: refused
     (dict(N=2**22, d=256, dtype=2), 2),
     (dict(N=2**21, d=256, dtype=0), 2),
 ])
@@ -247,3 +248,5 @@ def test_valid_call_without_a_device_reports_hip_error(lib):
     # returns FA_ERR_HIP without launching anything
     assert call(lib) == 8
     assert lib.fa_last_hip_error() != 0
+    # the longest head the checks accept at d = 128 (one tile short of 2^31 bytes)
+    assert call(lib, N=2**23 - 512, d=128, dtype=2) == 8

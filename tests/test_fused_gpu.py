@@ -221,3 +221,33 @@ def test_workload_many_rows(name, nrows):
     rows = spread_rows(w.B, w.H, w.N, nrows, seed=w.seed)
     assert len(rows) >= nrows
     _compare_rows(name, w, o, lse, x, rows)
+
+
+def test_longest_accepted_head():
+    # the largest head the boundary accepts for 16-bit inputs at d = 128: one head of Q, K
+    # or V may take 2^31 - 2^17 bytes (the buffer-descriptor range less one tile), so
+    # N = 2^23 - 512 (N + 1 is refused, a CPU test checks that) and O is ~4 GiB; 32766
+    # query tiles of 131064 key tiles each.  Rows at both ends, at tile and workgroup
+    # edges and at random against the oracle (~4 GFLOP of fp64 per row).
+    import torch
+
+    B, H, N, d, dtype = 1, 1, 2**23 - 512, 128, "bf16"
+    scale32 = float(np.float32(1.0 / math.sqrt(d)))
+    say(f"longest head: generating bf16 B1 H1 N{N} d{d}")
+    x = make_qkv(B, H, N, d, dtype, seed=2323)
+    say("longest head: fused kernel (~40 s)")
+    o, lse = run("fused", to_device(x, dtype), scale32)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(23))
+    fixed = [0, 1, 31, 32, 63, 64, 255, 256, N // 2, N - 257, N - 256, N - 65, N - 64,
+             N - 33, N - 32, N - 2, N - 1]
+    rows = np.array(sorted(set(fixed) | set(int(i) for i in rng.integers(0, N, size=31))),
+                    np.int64)
+    say(f"longest head: oracle on {len(rows)} rows")
+    o_ref, lse_ref = oracle.attention(x["q"], x["k"], x["v"], dtype, scale32, rows=rows)
+    idx = torch.from_numpy(rows).to(o.device)
+    m = metrics(o.reshape(-1, d).index_select(0, idx).cpu().numpy(),
+                lse.reshape(-1).index_select(0, idx).cpu().numpy(), o_ref, lse_ref)
+    say(f"longest head: {m}")
+    assert_parity(m, dtype, where="N = 2^23 - 512")
+    assert bool(torch.isfinite(lse).all())
