@@ -164,14 +164,27 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, 
 // waits explicitly (s_waitcnt vmcnt) for exactly the loads a barrier publishes.  The
 // compiler's own waits for the loads it tracks stay correct: loads retire in order, so
 // extra untracked loads can only make those waits longer.
+//
+// Nor does the compiler keep, before inline assembly, the 5 wait states a vector-memory
+// instruction needs after a vector instruction writes one of its scalar operands (a
+// scalar restored from a spill with v_readlane, for instance).  SAFE = true puts them in
+// front of the load, for kernels whose scalar registers spill; the assembly hazard test
+// checks every kernel for both forms.
+template <bool SAFE = false>
 __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char *lds_wave_base,
                                                int voff, int soff) {
   const uint32_t m0v =
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_wave_base;
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-               :
-               : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0v)
-               : "memory");
+  if constexpr (SAFE)
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0v)
+                 : "memory");
+  else
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(r), "s"(soff), "{m0}"(m0v)
+                 : "memory");
 }
 
 // Workgroup barrier that orders LDS accesses only: the loads into LDS above are not

@@ -52,6 +52,8 @@ struct Cfg16 {
   static constexpr int OB = D / 32;             // 32-wide blocks of the output
   static constexpr int PU = BN / 16;            // k-steps of the P V product
   static constexpr int LDS = 4 * TILEB;         // K and V, two stages each
+  static constexpr int QB = BM * ROWB;          // bytes of a Q tile
+  static constexpr int LDSP = LDS + QB;         // persistent form: plus a Q region
   // minimum waves per SIMD the registers must allow: at d = 256 one 32-row wave holds
   // O (128 registers) and Q (64), and a wave of two 32-row blocks at d = 128 holds two
   // of each; both need more than half of the register file.  Two 32-row blocks at d = 64
@@ -83,7 +85,14 @@ struct Cfg16 {
 // STATS: the statistics-recording form (validation only, nsplit = 1): after every key
 // tile t each query row's running max (base-2 units, c m) and row sum go to
 // ST[((b H + h) N + i) ceil(N/64) + t][0..1].  The other forms ignore ST.
-template <int D, bool BF16, int WAVES, int RB, bool STATS = false>
+//
+// PERSIST: the persistent form (nsplit = 1, at least two key tiles, no STATS).  The grid
+// holds fewer workgroups than the G tiles and workgroup b takes tiles b, b + gridDim.x,
+// b + 2 gridDim.x, ... in turn.  The next tile's Q (into an LDS region of its own) and its
+// first K and V tiles are loaded while the current tile's last key tiles are processed, so
+// that a new tile starts without waiting for memory, and its output goes out through the
+// Q region while the next tile's first K/V tiles sit in the stages.
+template <int D, bool BF16, int WAVES, int RB, bool STATS = false, bool PERSIST = false>
 __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
     const uint16_t *__restrict__ V, float *__restrict__ O, float *__restrict__ LSE, int N,
@@ -103,6 +112,9 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *const Ks = smem;
   char *const Vs = smem + 2 * C::TILEB;
+  // the Q tile is staged in the K stages, or in the persistent form in a region of its own
+  char *const Qs = PERSIST ? smem + C::LDS : smem;
+  static_assert(!PERSIST || !STATS, "the persistent form records no statistics");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -110,18 +122,44 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // Key range g holds keys [g kps, min(N, (g + 1) kps)); its result (O normalised over
   // those keys, and their LSE) goes to slot g of O and LSE, whose slots are B H N d and
   // B H N values apart.  With nsplit = 1 (kps = N) that is the whole attention.
-  const int L = xcd_remap(blockIdx.x, G);
-  const int qt = L % nqt, kg = (L / nqt) % nsplit, bh = L / nqt / nsplit;
-  const int q0 = qt * C::BM;
-  const int64_t hoff = int64_t(bh) * N * D;
   const int64_t bhn = int64_t(G / (nqt * nsplit)) * N;  // rows of one output slot
-  const int kbeg = kg * kps, NK = min(N - kbeg, kps);    // keys of this range, >= 1
+  const uint32_t head_bytes = uint32_t(N) * C::ROWB;
+  int vt = blockIdx.x;  // the workgroup's tile (in the persistent form, the current one)
+  int qt, kg, bh, q0, kbeg;
+  int64_t hoff;
   // buffer resources over this head's [N, D] slices (K and V: the range's rows): loads
   // past the last row read zeros
-  const uint32_t head_bytes = uint32_t(N) * C::ROWB;
-  const auto qrs = make_rsrc(Q + hoff, head_bytes);
-  const auto krs = make_rsrc(K + hoff + int64_t(kbeg) * D, uint32_t(NK) * C::ROWB);
-  const auto vrs = make_rsrc(V + hoff + int64_t(kbeg) * D, uint32_t(NK) * C::ROWB);
+  __amdgpu_buffer_rsrc_t qrs, krs, vrs;
+  auto set_tile = [&](int v) __attribute__((always_inline)) {
+    const int L = xcd_remap(v, G);
+    qt = L % nqt;
+    kg = (L / nqt) % nsplit;
+    bh = L / nqt / nsplit;
+    q0 = qt * C::BM;
+    hoff = int64_t(bh) * N * D;
+    kbeg = kg * kps;
+    const int nk = min(N - kbeg, kps);  // keys of this range, >= 1
+    qrs = make_rsrc(Q + hoff, head_bytes);
+    krs = make_rsrc(K + hoff + int64_t(kbeg) * D, uint32_t(nk) * C::ROWB);
+    vrs = make_rsrc(V + hoff + int64_t(kbeg) * D, uint32_t(nk) * C::ROWB);
+  };
+  set_tile(vt);
+  // keys of the range (in the persistent form, nsplit = 1: N for every tile)
+  const int NK = min(N - kbeg, kps);
+  // persistent form: the next tile (or, for the last tile of the workgroup, the current
+  // one again: its loads then land in LDS regions that nothing reads any more)
+  bool has_next = false;
+  int q0n = 0;
+  __amdgpu_buffer_rsrc_t qrn = qrs, krn = krs, vrn = vrs;
+  auto set_next = [&]() __attribute__((always_inline)) {
+    has_next = vt + int(gridDim.x) < G;
+    const int L = xcd_remap(has_next ? vt + int(gridDim.x) : vt, G);
+    const int64_t ho = int64_t(L / nqt) * N * D;
+    q0n = (L % nqt) * C::BM;
+    qrn = make_rsrc(Q + ho, head_bytes);
+    krn = make_rsrc(K + ho, head_bytes);
+    vrn = make_rsrc(V + ho, head_bytes);
+  };
   constexpr int ST_STEP = C::NT * 16;  // bytes between a thread's chunks, in LDS and memory
   // A tile of rows is one contiguous block of global memory: thread tid moves the
   // 16-byte chunks tid + NT i.  Their LDS rows differ by NT/CPR per i, which leaves
@@ -136,17 +174,20 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // ---- prologue: Q tile -> LDS (coalesced 16-byte loads) -> registers ----
 #pragma unroll
   for (int i = 0; i < C::QCPT; ++i)
-    lds_write16(Ks, st_ki(i) + i * ST_STEP, buf_load16(qrs, tid * 16, q0 * C::ROWB + i * ST_STEP));
+    lds_write16(Qs, st_ki(i) + i * ST_STEP, buf_load16(qrs, tid * 16, q0 * C::ROWB + i * ST_STEP));
   __syncthreads();
   // block r of wave w holds query rows 32 (RB w + r) .. +31 of the tile
   u32x4 qf[RB][C::KC];
+  auto read_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const int qr = 32 * (RB * w + r) + l32;
+    for (int r = 0; r < RB; ++r) {
+      const int qr = 32 * (RB * w + r) + l32;
 #pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc)
-      qf[r][kc] = lds_read16(Ks, qr * C::ROWB + swz_row<C::CPR>(qr, 2 * kc + h) * 16);
-  }
+      for (int kc = 0; kc < C::KC; ++kc)
+        qf[r][kc] = lds_read16(Qs, qr * C::ROWB + swz_row<C::CPR>(qr, 2 * kc + h) * 16);
+    }
+  };
+  read_q();
   __syncthreads();
 
   // ---- per-lane LDS offsets, fixed for the whole loop ----
@@ -185,21 +226,36 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   auto dma_k = [&](char *kb, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      buf_load16_lds(krs, kb + dma_wave + i * ST_STEP, st_ki(i), kt * C::TILEB + i * ST_STEP);
+      buf_load16_lds<PERSIST>(krs, kb + dma_wave + i * ST_STEP, st_ki(i), kt * C::TILEB + i * ST_STEP);
   };
   auto dma_v = [&](char *vb, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      buf_load16_lds(vrs, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB + i * ST_STEP);
+      buf_load16_lds<PERSIST>(vrs, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB + i * ST_STEP);
   };
   // one chunk of a tile's load: an iteration's loads ride one per step between its
   // first matrix-core steps instead of all issuing before them (measured: bitwise the
   // same results, +2.7 % at bf16 8x32x4096x128, +3.9 % at d = 256)
-  auto dma_k1 = [&](char *kb, int kt, int i) __attribute__((always_inline)) {
-    buf_load16_lds(krs, kb + dma_wave + i * ST_STEP, st_ki(i), kt * C::TILEB + i * ST_STEP);
+  // (safe: the form that keeps the scalar operands' wait states, for the steps where the
+  // persistent form restores spilled scalars; the steady-state loop has none)
+  auto dma_k1 = [&](char *kb, int kt, int i, auto safe) __attribute__((always_inline)) {
+    buf_load16_lds<decltype(safe)::value>(krs, kb + dma_wave + i * ST_STEP, st_ki(i),
+                                          kt * C::TILEB + i * ST_STEP);
   };
-  auto dma_v1 = [&](char *vb, int kt, int i) __attribute__((always_inline)) {
-    buf_load16_lds(vrs, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB + i * ST_STEP);
+  auto dma_v1 = [&](char *vb, int kt, int i, auto safe) __attribute__((always_inline)) {
+    buf_load16_lds<decltype(safe)::value>(vrs, vb + dma_wave + i * ST_STEP, st_v,
+                                          kt * C::TILEB + i * ST_STEP);
+  };
+  // the persistent form's loads of the next tile: chunk i of its K or V tile kt, and
+  // chunk i of its Q tile into the Q region (the same swizzled layout as the Q prologue)
+  auto dma_kn = [&](char *kb, int kt, int i) __attribute__((always_inline)) {
+    buf_load16_lds<PERSIST>(krn, kb + dma_wave + i * ST_STEP, st_ki(i), kt * C::TILEB + i * ST_STEP);
+  };
+  auto dma_vn = [&](char *vb, int kt, int i) __attribute__((always_inline)) {
+    buf_load16_lds<PERSIST>(vrn, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB + i * ST_STEP);
+  };
+  auto dma_qn = [&](int i) __attribute__((always_inline)) {
+    buf_load16_lds<PERSIST>(qrn, Qs + dma_wave + i * ST_STEP, st_ki(i), q0n * C::ROWB + i * ST_STEP);
   };
   // bfloat16 V: the P V product runs in binary16, so each thread widens the chunks its
   // own loads wrote (chunk i: 16 bytes at dma_wave + i ST_STEP + 16 lane), in place.
@@ -490,144 +546,216 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   dma_k(Ks, 0);
   dma_v(Vs, 0);
   dma_k(Ks + C::TILEB, 1);
-  wait_loads(in_flight_1{});  // K_0 and V_0 have landed
+  // K_0 and V_0 have landed (persistent form: K_1 too, as for every later tile)
+  if constexpr (PERSIST)
+    wait_loads(in_flight_0{});
+  else
+    wait_loads(in_flight_1{});
   if constexpr (BF16) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) widen_v(Vs, i);
   }
   lds_barrier();
+  // LDS stage of the tile's K_0 and V_0: K_j and V_j sit in stage (j + sb) % 2.  In the
+  // persistent form the stages alternate across tiles as if their key tiles were one
+  // sequence, so that the next tile's first tiles go to the stages the current tile's
+  // last ones have left.
+  int sb = 0;
+  static_assert(!PERSIST || (!ASMPV && C::QB >= 32 * D * 4 * RB / 2),
+                "persistent form: O in vector registers, its output staged in the Q region");
+  for (;;) {
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const u32x4 kop = k_op(k_base, i);
+    for (int i = 0; i < NA; ++i) {
+      const u32x4 kop = k_op(k_base + sb * C::TILEB, i);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) s_step(i, kop, r);
-  }
-  if (nkt == 1 && nlast < C::BN) mask(nlast);
-  if constexpr (EARLY_MAX) {
-#pragma unroll
-    for (int k = 0; k < NAM; ++k)
-#pragma unroll
-      for (int r = 0; r < RB; ++r) max_a(k, r);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int k = 0; k < NB; ++k) {
-#pragma unroll
-    for (int r = 0; r < RB; ++r) soft_b(k, r);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // K_1 has landed, and every wave is done with K_0 before stage 0 is refilled
-  wait_loads(in_flight_0{});
-  lds_barrier();
-
-  // ---- steady state: iteration j (P = j % 2 selects the LDS stages) ----
-  //   A: V_{j+1} and K_{j+2} start towards LDS; S_{j+1} = K_{j+1} Q^T on the matrix
-  //      cores, while the VALU finishes the softmax of tile j and rescales O by alpha_j
-  //   B: O += V_j P_j on the matrix cores, while the VALU starts the softmax of S_{j+1}
-  //      and widens bfloat16 V_{j+1}
-  // The stages written in iteration j held K_j and V_{j-1}, last read in iteration j-1;
-  // the barrier that ends each iteration orders every stage's last read before its next
-  // write, and every write before its next read: before it each wave waits for its loads
-  // of V_{j+1} and K_{j+2}, which iteration j + 1 reads.  B waits for V_{j+1} alone (it
-  // was issued first) before widening it, and the transposing reads of V_j wait for
-  // nothing.
-  // MASKED: the tile started in this iteration (j + 1) is the last one, so its keys past
-  // N are masked; only the final iteration is compiled with it, keeping the mask out of
-  // the steady-state loop
-  auto iter = [&](int j, auto masked) __attribute__((always_inline)) {
-    constexpr bool MASKED = decltype(masked)::value;
-    const int P = j & 1;
-    // lane bases of this iteration's reads (the pins keep the offset arithmetic inside
-    // the loop rather than precomputed into live registers)
-    pin(k_xor);
-    pin(v_xor);
-    const int kb = k_base + (1 - P) * C::TILEB;         // K_{j+1}
-    const int vb = v_base + (2 + P) * C::TILEB;         // V_j
-    char *vw = Vs + (1 - P) * C::TILEB;                 // V_{j+1}, widened in B
-    char *kw = Ks + P * C::TILEB;                       // K_{j+2}
-
-    // ---- A ----
-    st_tile = j;
-    rescale_lazy();
-#pragma unroll
-    for (int i = 0; i < DK; ++i) kf[i] = k_op(kb, i);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NA; ++i)
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        s_step(i, kf[i % DK], r);
-        if (r == RB - 1 && i + DK < NA) kf[i % DK] = k_op(kb, i + DK);
-        // V_{j+1} first (B waits for it alone), then K_{j+2}
-        if (r == 0 && i < CPT) dma_v1(vw, j + 1, i);
-        if (r == 0 && i >= CPT && i < 2 * CPT) dma_k1(kw, j + 2, i - CPT);
-        // the last tile's keys past N are masked before its early max reads key block 0
-        if (EARLY_MAX && MASKED && i == KC + 1 && r == 0 && nlast < C::BN)
-          mask_block(0, nlast);
-        soft_a(i, r);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-
-    // ---- B ----
-#pragma unroll
-    for (int i = 0; i < DV; ++i) vf[i] = v_op(vb, i);
-    if (MASKED && nlast < C::BN) mask(nlast);
-    // bfloat16 V_{j+1} is widened in place during the P V product below, once this
-    // wave's loads of it have landed (the loads issued after it may stay in flight)
-    if constexpr (BF16) wait_loads(in_flight_1{});
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        pv_step(i, vf[i % DV], r);
-        if (r == RB - 1 && i + DV < NB) vf[i % DV] = v_op(vb, i + DV);
-        soft_b(i, r);
-        {
-          // chunk c: read at step (NB / CPT) c + 1, widened and written back at the
-          // chunk's last step
-          if (r == 0 && i % (NB / CPT) == 1) widen_read(vw, i / (NB / CPT));
-          if (r == RB - 1 && i % (NB / CPT) == NB / CPT - 1) widen_write(vw, i / (NB / CPT));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    settle_o();
-    wait_loads(in_flight_0{});
-    lds_barrier();
-  };
-
-  for (int j = 0; j + 2 < nkt; ++j) iter(j, std::false_type{});
-  if (nkt >= 2) iter(nkt - 2, std::true_type{});
-
-  // ---- last tile T = nkt - 1: the A share of its softmax, then its P V product ----
-  {
-    const int vb = v_base + (2 + ((nkt - 1) & 1)) * C::TILEB;
-    st_tile = nkt - 1;
-    rescale_lazy();
-#pragma unroll
-    for (int k = 0; k < NA; ++k)
-#pragma unroll
-      for (int r = 0; r < RB; ++r) soft_a(k, r, false);
-    if constexpr (ASMPV) mfma_drain();
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const u32x4 vop = v_op(vb, i);
-#pragma unroll
-      for (int r = 0; r < RB; ++r) pv_step(i, vop, r);
+      for (int r = 0; r < RB; ++r) s_step(i, kop, r);
     }
-    settle_o();
-  }
-
-  // every wave is done with the K/V stages before they hold the output
-  lds_barrier();
-  constexpr int WAVE_LDS = C::LDS / WAVES;                 // bytes of a wave's region
-  constexpr int NHALF = (32 * D * 4 + WAVE_LDS - 1) / WAVE_LDS;
+    if (nkt == 1 && nlast < C::BN) mask(nlast);
+    if constexpr (EARLY_MAX) {
 #pragma unroll
-  for (int r = 0; r < RB; ++r) {
-    const int row0 = q0 + 32 * (RB * w + r);  // the block's first query row
-    store_rows_lds<D, NHALF>(o[r], mc[r], l[r], LAZY ? lp[r] : l[r], smem + w * WAVE_LDS,
-                             O + kg * bhn * D + hoff + int64_t(row0) * D,
-                             LSE + kg * bhn + int64_t(bh) * N + row0, lane, N - row0);
+      for (int k = 0; k < NAM; ++k)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) max_a(k, r);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) soft_b(k, r);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // K_1 has landed, and every wave is done with K_0 before its stage is refilled
+    if constexpr (!PERSIST) wait_loads(in_flight_0{});
+    lds_barrier();
+
+    // ---- steady state: iteration j (P = (j + sb) % 2 selects the LDS stages) ----
+    //   A: V_{j+1} and K_{j+2} start towards LDS; S_{j+1} = K_{j+1} Q^T on the matrix
+    //      cores, while the VALU finishes the softmax of tile j and rescales O by alpha_j
+    //   B: O += V_j P_j on the matrix cores, while the VALU starts the softmax of S_{j+1}
+    //      and widens bfloat16 V_{j+1}
+    // The stages written in iteration j held K_j and V_{j-1}, last read in iteration j-1;
+    // the barrier that ends each iteration orders every stage's last read before its next
+    // write, and every write before its next read: before it each wave waits for its
+    // loads of V_{j+1} and K_{j+2}, which iteration j + 1 reads.  B waits for V_{j+1}
+    // alone (it was issued first) before widening it, and the transposing reads of V_j
+    // wait for nothing.
+    // MASKED: the tile started in this iteration (j + 1) is the last one, so its keys past
+    // N are masked; only the final iteration is compiled with it, keeping the mask out of
+    // the steady-state loop.  In the persistent form that iteration loads the next tile's
+    // K_0 in place of K_{j+2} (past the end), then the next tile's Q, which its waits leave
+    // in flight.
+    auto iter = [&](int j, auto masked) __attribute__((always_inline)) {
+      constexpr bool MASKED = decltype(masked)::value;
+      constexpr bool NEXT = PERSIST && MASKED;
+      constexpr int QSTEPS = NA - 2 * CPT;  // A steps that carry the next tile's Q
+      static_assert(!NEXT || QSTEPS >= 1, "the next tile's Q needs A steps of its own");
+      const int P = (j + sb) & 1;
+      // lane bases of this iteration's reads (the pins keep the offset arithmetic inside
+      // the loop rather than precomputed into live registers)
+      pin(k_xor);
+      pin(v_xor);
+      const int kb = k_base + (1 - P) * C::TILEB;         // K_{j+1}
+      const int vb = v_base + (2 + P) * C::TILEB;         // V_j
+      char *vw = Vs + (1 - P) * C::TILEB;                 // V_{j+1}, widened in B
+      char *kw = Ks + P * C::TILEB;                       // K_{j+2}
+
+      // ---- A ----
+      st_tile = j;
+      rescale_lazy();
+#pragma unroll
+      for (int i = 0; i < DK; ++i) kf[i] = k_op(kb, i);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NA; ++i)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          s_step(i, kf[i % DK], r);
+          if (r == RB - 1 && i + DK < NA) kf[i % DK] = k_op(kb, i + DK);
+          // V_{j+1} first (B waits for it alone), then K_{j+2}
+          if (r == 0 && i < CPT) dma_v1(vw, j + 1, i, std::integral_constant<bool, NEXT>{});
+          if (r == 0 && i >= CPT && i < 2 * CPT) {
+            if constexpr (NEXT)
+              dma_kn(kw, 0, i - CPT);
+            else
+              dma_k1(kw, j + 2, i - CPT, std::false_type{});
+          }
+          if constexpr (NEXT) {
+#pragma unroll
+            for (int q = 0; q < C::QCPT; ++q)
+              if (r == 0 && i >= 2 * CPT && q * QSTEPS / C::QCPT == i - 2 * CPT) dma_qn(q);
+          }
+          // the last tile's keys past N are masked before its early max reads key block 0
+          if (EARLY_MAX && MASKED && i == KC + 1 && r == 0 && nlast < C::BN)
+            mask_block(0, nlast);
+          soft_a(i, r);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+
+      // ---- B ----
+#pragma unroll
+      for (int i = 0; i < DV; ++i) vf[i] = v_op(vb, i);
+      if (MASKED && nlast < C::BN) mask(nlast);
+      // bfloat16 V_{j+1} is widened in place during the P V product below, once this
+      // wave's loads of it have landed (the loads issued after it may stay in flight)
+      if constexpr (BF16) {
+        if constexpr (NEXT)
+          wait_loads(std::integral_constant<int, CPT + C::QCPT>{});
+        else
+          wait_loads(in_flight_1{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+          pv_step(i, vf[i % DV], r);
+          if (r == RB - 1 && i + DV < NB) vf[i % DV] = v_op(vb, i + DV);
+          soft_b(i, r);
+          {
+            // chunk c: read at step (NB / CPT) c + 1, widened and written back at the
+            // chunk's last step
+            if (r == 0 && i % (NB / CPT) == 1) widen_read(vw, i / (NB / CPT));
+            if (r == RB - 1 && i % (NB / CPT) == NB / CPT - 1) widen_write(vw, i / (NB / CPT));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      settle_o();
+      if constexpr (NEXT)
+        wait_loads(std::integral_constant<int, C::QCPT>{});  // the next tile's Q may fly on
+      else
+        wait_loads(in_flight_0{});
+      lds_barrier();
+    };
+
+    for (int j = 0; j + 2 < nkt; ++j) iter(j, std::false_type{});
+    if constexpr (PERSIST) set_next();  // (here, so that its registers are not held in the loop)
+    if (nkt >= 2) iter(nkt - 2, std::true_type{});
+
+    // ---- last tile T = nkt - 1: the A share of its softmax, then its P V product ----
+    // (persistent form: the next tile's V_0 and K_1 go to the stages that V_{T-1} and K_T
+    // have left)
+    const int sbn = (sb + nkt) & 1;  // the next tile's stage base
+    {
+      if constexpr (PERSIST) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) dma_vn(Vs + sbn * C::TILEB, 0, i);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) dma_kn(Ks + (1 - sbn) * C::TILEB, 1, i);
+      }
+      const int vb = v_base + (2 + ((nkt - 1 + sb) & 1)) * C::TILEB;
+      st_tile = nkt - 1;
+      rescale_lazy();
+#pragma unroll
+      for (int k = 0; k < NA; ++k)
+#pragma unroll
+        for (int r = 0; r < RB; ++r) soft_a(k, r, false);
+      if constexpr (ASMPV) mfma_drain();
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const u32x4 vop = v_op(vb, i);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) pv_step(i, vop, r);
+      }
+      settle_o();
+    }
+
+    if constexpr (PERSIST) {
+      // the next tile's Q, K_0, V_0 and K_1 have landed; this thread widens its own
+      // chunks of V_0, then (after the barrier) every wave takes its Q rows, and after a
+      // second barrier the Q region holds the output on its way out
+      wait_loads(in_flight_0{});
+      if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) widen_v(Vs + sbn * C::TILEB, i);
+      }
+      lds_barrier();
+      if (has_next) read_q();
+    }
+    // every wave is done with the LDS region that holds the output (the K/V stages, or in
+    // the persistent form the Q region)
+    lds_barrier();
+    constexpr int WAVE_LDS = (PERSIST ? C::QB : C::LDS) / WAVES;  // bytes of a wave's region
+    constexpr int NHALF = (32 * D * 4 + WAVE_LDS - 1) / WAVE_LDS;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int row0 = q0 + 32 * (RB * w + r);  // the block's first query row
+      store_rows_lds<D, NHALF>(o[r], mc[r], l[r], LAZY ? lp[r] : l[r], Qs + w * WAVE_LDS,
+                               O + kg * bhn * D + hoff + int64_t(row0) * D,
+                               LSE + kg * bhn + int64_t(bh) * N + row0, lane, N - row0);
+    }
+    if (!PERSIST || !has_next) break;
+
+    // ---- the next tile: fresh online-softmax state and output accumulators ----
+    vt += gridDim.x;
+    set_tile(vt);
+    sb = sbn;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+#pragma unroll
+      for (int e = 0; e < OB; ++e) o[r][e] = f32x16{};
+      mc[r] = -INFINITY;
+      l[r] = alpha[r] = rs[r] = lp[r] = rp[r] = 0.f;
+    }
   }
 }
 
@@ -635,17 +763,36 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
 // nsplit key ranges of kps keys each (the last may be shorter, none is empty); with
 // nsplit = 1 and kps = N the kernel writes the attention itself to o and lse
 // STATS: the statistics-recording form, writing to stats (nsplit = 1).
+// With nsplit = 1, at least two key tiles, d = 128 and more tiles than the device holds
+// workgroups at once, the persistent form runs instead: one workgroup per resident slot,
+// each taking its tiles in turn.
 template <int D, bool BF16, int WAVES, int RB, bool STATS = false>
 inline hipError_t run16(const Problem &p, float *o, float *lse, int nsplit, int kps,
                         hipStream_t stream, float *stats = nullptr) {
   using C = Cfg16<D, WAVES, RB>;
+  const int nqt = (p.N + C::BM - 1) / C::BM;
+  const int G = nqt * p.B * p.H * nsplit;
+  const float c = p.scale * kLog2e;
+  if constexpr (!STATS && D == 128) {
+    if (nsplit == 1 && p.N > C::BN) {
+      constexpr auto pk = fa_fwd16_kernel<D, BF16, WAVES, RB, false, true>;
+      const int R = resident_workgroups<pk>(C::NT, C::LDSP);
+      if (R >= 8 && G > R) {
+        const hipError_t ea = allow_lds_on_device<pk>(C::LDSP);
+        if (ea != hipSuccess) return ea;
+        // a multiple of 8, so that workgroup b keeps the XCD (b mod 8) of all its tiles
+        hipLaunchKernelGGL(pk, dim3(R & ~7), dim3(C::NT), C::LDSP, stream,
+                           static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
+                           static_cast<const uint16_t *>(p.v), o, lse, p.N, nqt, G, c, 1, p.N,
+                           stats);
+        return hipGetLastError();
+      }
+    }
+  }
   auto kern = fa_fwd16_kernel<D, BF16, WAVES, RB, STATS>;
   const hipError_t ea =
       allow_lds_on_device<fa_fwd16_kernel<D, BF16, WAVES, RB, STATS>>(C::LDS);
   if (ea != hipSuccess) return ea;
-  const int nqt = (p.N + C::BM - 1) / C::BM;
-  const int G = nqt * p.B * p.H * nsplit;
-  const float c = p.scale * kLog2e;
   hipLaunchKernelGGL(kern, dim3(G), dim3(C::NT), C::LDS, stream,
                      static_cast<const uint16_t *>(p.q), static_cast<const uint16_t *>(p.k),
                      static_cast<const uint16_t *>(p.v), o, lse, p.N, nqt, G, c, nsplit, kps,

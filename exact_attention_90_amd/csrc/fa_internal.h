@@ -60,6 +60,32 @@ inline hipError_t allow_lds_on_device(int bytes) {
   return e;
 }
 
+// Workgroups of kernel Kern (nt threads, lds bytes of LDS) the current device holds at
+// once: compute units x resident workgroups per compute unit, found once per device (ids
+// 0..63; beyond that on every call).  0 when the device cannot say.
+template <auto Kern>
+inline int resident_workgroups(int nt, int lds) {
+  static std::atomic<int> known[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const bool cached = dev >= 0 && dev < 64;
+  if (cached) {
+    const int v = known[dev].load(std::memory_order_acquire);
+    if (v > 0) return v;
+  }
+  int ncu = 0, per = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (hipFuncSetAttribute(reinterpret_cast<const void *>(Kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, Kern, nt, size_t(lds)) != hipSuccess)
+    return 0;
+  const int v = ncu * per;
+  if (cached && v > 0) known[dev].store(v, std::memory_order_release);
+  return v > 0 ? v : 0;
+}
+
 hipError_t launch_fused(const Problem &p, hipStream_t stream);
 // the 16-bit kernels (binary16 / bfloat16 inputs): key ranges as in launch_fused_split,
 // written to o and lse (nsplit = 1, kps = N: the attention itself); d = 128 lives in
