@@ -146,8 +146,9 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   set_tile(vt);
   // keys of the range (in the persistent form, nsplit = 1: N for every tile)
   const int NK = min(N - kbeg, kps);
-  // persistent form: the next tile (or, for the last tile of the workgroup, the current
-  // one again: its loads then land in LDS regions that nothing reads any more)
+  // persistent form: the next tile.  For the workgroup's last tile the same loads are
+  // issued (so that every wait counts the same loads) over an empty buffer range: they
+  // read nothing from memory and write zeros to LDS regions that nothing reads any more.
   bool has_next = false;
   int q0n = 0;
   __amdgpu_buffer_rsrc_t qrn = qrs, krn = krs, vrn = vrs;
@@ -155,10 +156,11 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
     has_next = vt + int(gridDim.x) < G;
     const int L = xcd_remap(has_next ? vt + int(gridDim.x) : vt, G);
     const int64_t ho = int64_t(L / nqt) * N * D;
+    const uint32_t nb = has_next ? head_bytes : 0u;
     q0n = (L % nqt) * C::BM;
-    qrn = make_rsrc(Q + ho, head_bytes);
-    krn = make_rsrc(K + ho, head_bytes);
-    vrn = make_rsrc(V + ho, head_bytes);
+    qrn = make_rsrc(Q + ho, nb);
+    krn = make_rsrc(K + ho, nb);
+    vrn = make_rsrc(V + ho, nb);
   };
   constexpr int ST_STEP = C::NT * 16;  // bytes between a thread's chunks, in LDS and memory
   // A tile of rows is one contiguous block of global memory: thread tid moves the
