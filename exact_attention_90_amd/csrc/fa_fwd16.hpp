@@ -53,7 +53,9 @@ struct Cfg16 {
   static constexpr int PU = BN / 16;            // k-steps of the P V product
   static constexpr int LDS = 4 * TILEB;         // K and V, two stages each
   static constexpr int QB = BM * ROWB;          // bytes of a Q tile
-  static constexpr int LDSP = LDS + QB;         // persistent form: plus a Q region
+  // persistent form: plus a Q region (d = 256: half of one, beside 128 KiB of K/V stages
+  // in the 160 KiB of LDS; the other half of the next Q goes to a K stage)
+  static constexpr int LDSP = LDS + (D == 256 ? QB / 2 : QB);
   // minimum waves per SIMD the registers must allow: at d = 256 one 32-row wave holds
   // O (128 registers) and Q (64), and a wave of two 32-row blocks at d = 128 holds two
   // of each; both need more than half of the register file.  Two 32-row blocks at d = 64
@@ -112,8 +114,13 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *const Ks = smem;
   char *const Vs = smem + 2 * C::TILEB;
-  // the Q tile is staged in the K stages, or in the persistent form in a region of its own
-  char *const Qs = PERSIST ? smem + C::LDS : smem;
+  // the Q tile is staged in the K stages, or in the persistent form at d = 128 in a region
+  // of its own.  QSPLIT (the persistent form at d = 256): the next tile's Q rows 0 .. BM/2-1
+  // go to the region past the K/V stages (Xs, half a Q tile), rows BM/2 .. BM-1 to the K
+  // stage its last key tile has left.
+  constexpr bool QSPLIT = PERSIST && D == 256;
+  char *const Qs = (PERSIST && !QSPLIT) ? smem + C::LDS : smem;
+  constexpr int XS_OFF = C::LDS;  // byte offset of Xs in LDS
   static_assert(!PERSIST || !STATS, "the persistent form records no statistics");
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -180,16 +187,18 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   __syncthreads();
   // block r of wave w holds query rows 32 (RB w + r) .. +31 of the tile
   u32x4 qf[RB][C::KC];
-  auto read_q = [&]() __attribute__((always_inline)) {
+  // base: LDS byte offset of the tile's row 0 (row qr at base + qr ROWB, swizzled chunks)
+  auto read_q = [&](int base) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const int qr = 32 * (RB * w + r) + l32;
 #pragma unroll
       for (int kc = 0; kc < C::KC; ++kc)
-        qf[r][kc] = lds_read16(Qs, qr * C::ROWB + swz_row<C::CPR>(qr, 2 * kc + h) * 16);
+        qf[r][kc] =
+            lds_read16(smem, base + qr * C::ROWB + swz_row<C::CPR>(qr, 2 * kc + h) * 16);
     }
   };
-  read_q();
+  read_q(int(Qs - smem));
   __syncthreads();
 
   // ---- per-lane LDS offsets, fixed for the whole loop ----
@@ -256,8 +265,11 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   auto dma_vn = [&](char *vb, int kt, int i) __attribute__((always_inline)) {
     buf_load16_lds<PERSIST>(vrn, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB + i * ST_STEP);
   };
-  auto dma_qn = [&](int i) __attribute__((always_inline)) {
-    buf_load16_lds<PERSIST>(qrn, Qs + dma_wave + i * ST_STEP, st_ki(i), q0n * C::ROWB + i * ST_STEP);
+  // chunk i of the next Q tile (rows 8 i .. 8 i + 7 at d = 256) to LDS offset
+  // base + i ST_STEP; for QSPLIT the caller passes the base of the chunk's half
+  auto dma_qn = [&](int base, int i) __attribute__((always_inline)) {
+    buf_load16_lds<PERSIST>(qrn, smem + (base + i * ST_STEP + dma_wave), st_ki(i),
+                            q0n * C::ROWB + i * ST_STEP);
   };
   // bfloat16 V: the P V product runs in binary16, so each thread widens the chunks its
   // own loads wrote (chunk i: 16 bytes at dma_wave + i ST_STEP + 16 lane), in place.
@@ -563,8 +575,8 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // sequence, so that the next tile's first tiles go to the stages the current tile's
   // last ones have left.
   int sb = 0;
-  static_assert(!PERSIST || (!ASMPV && C::QB >= 32 * D * 4 * RB / 2),
-                "persistent form: O in vector registers, its output staged in the Q region");
+  static_assert(!PERSIST || (RB == 1 && (D == 128 || D == 256)),
+                "persistent form: one 32-row block per wave, d = 128 or 256");
   for (;;) {
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
@@ -587,7 +599,9 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
       __builtin_amdgcn_sched_barrier(0);
     }
     // K_1 has landed, and every wave is done with K_0 before its stage is refilled
-    if constexpr (!PERSIST) wait_loads(in_flight_0{});
+    // (persistent form at d = 128: K_1 landed before the previous barrier; at d = 256 it was
+    // issued after the previous tile's Q left its K stage)
+    if constexpr (!PERSIST || QSPLIT) wait_loads(in_flight_0{});
     lds_barrier();
 
     // ---- steady state: iteration j (P = (j + sb) % 2 selects the LDS stages) ----
@@ -610,6 +624,8 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
       constexpr bool MASKED = decltype(masked)::value;
       constexpr bool NEXT = PERSIST && MASKED;
       constexpr int QSTEPS = NA - 2 * CPT;  // A steps that carry the next tile's Q
+      // chunks of the next Q issued here (QSPLIT: the half bound for Xs)
+      constexpr int QIN = QSPLIT ? C::QCPT / 2 : C::QCPT;
       static_assert(!NEXT || QSTEPS >= 1, "the next tile's Q needs A steps of its own");
       const int P = (j + sb) & 1;
       // lane bases of this iteration's reads (the pins keep the offset arithmetic inside
@@ -643,8 +659,9 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
           }
           if constexpr (NEXT) {
 #pragma unroll
-            for (int q = 0; q < C::QCPT; ++q)
-              if (r == 0 && i >= 2 * CPT && q * QSTEPS / C::QCPT == i - 2 * CPT) dma_qn(q);
+            for (int q = 0; q < QIN; ++q)
+              if (r == 0 && i >= 2 * CPT && q * QSTEPS / QIN == i - 2 * CPT)
+                dma_qn(QSPLIT ? XS_OFF : int(Qs - smem), q);
           }
           // the last tile's keys past N are masked before its early max reads key block 0
           if (EARLY_MAX && MASKED && i == KC + 1 && r == 0 && nlast < C::BN)
@@ -661,7 +678,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
       // wave's loads of it have landed (the loads issued after it may stay in flight)
       if constexpr (BF16) {
         if constexpr (NEXT)
-          wait_loads(std::integral_constant<int, CPT + C::QCPT>{});
+          wait_loads(std::integral_constant<int, CPT + QIN>{});
         else
           wait_loads(in_flight_1{});
       }
@@ -683,7 +700,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
         }
       settle_o();
       if constexpr (NEXT)
-        wait_loads(std::integral_constant<int, C::QCPT>{});  // the next tile's Q may fly on
+        wait_loads(std::integral_constant<int, QIN>{});  // the next tile's Q may fly on
       else
         wait_loads(in_flight_0{});
       lds_barrier();
@@ -694,15 +711,23 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
     if (nkt >= 2) iter(nkt - 2, std::true_type{});
 
     // ---- last tile T = nkt - 1: the A share of its softmax, then its P V product ----
-    // (persistent form: the next tile's V_0 and K_1 go to the stages that V_{T-1} and K_T
-    // have left)
+    // (persistent form: the next tile's V_0 goes to the stage V_{T-1} has left, and its K_1
+    // (d = 128) or the second half of its Q (d = 256) to the stage K_T has left)
     const int sbn = (sb + nkt) & 1;  // the next tile's stage base
+    // QSPLIT: LDS offset of the next Q's row 0 for its second half (rows BM/2 .. in the K
+    // stage K_T has left)
+    const int qhi = (1 - sbn) * C::TILEB - (C::QCPT / 2) * ST_STEP;
     {
       if constexpr (PERSIST) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) dma_vn(Vs + sbn * C::TILEB, 0, i);
+        if constexpr (QSPLIT) {
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) dma_kn(Ks + (1 - sbn) * C::TILEB, 1, i);
+          for (int q = C::QCPT / 2; q < C::QCPT; ++q) dma_qn(qhi, q);
+        } else {
+#pragma unroll
+          for (int i = 0; i < CPT; ++i) dma_kn(Ks + (1 - sbn) * C::TILEB, 1, i);
+        }
       }
       const int vb = v_base + (2 + ((nkt - 1 + sb) & 1)) * C::TILEB;
       st_tile = nkt - 1;
@@ -722,26 +747,42 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
     }
 
     if constexpr (PERSIST) {
-      // the next tile's Q, K_0, V_0 and K_1 have landed; this thread widens its own
-      // chunks of V_0, then (after the barrier) every wave takes its Q rows, and after a
-      // second barrier the Q region holds the output on its way out
+      // the next tile's Q, K_0, V_0 (and at d = 128 K_1) have landed; this thread widens
+      // its own chunks of V_0, then (after the barrier) every wave takes its Q rows, and
+      // after a second barrier the Q region holds the output on its way out
       wait_loads(in_flight_0{});
       if constexpr (BF16) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) widen_v(Vs + sbn * C::TILEB, i);
       }
       lds_barrier();
-      if (has_next) read_q();
+      if (has_next) {
+        if constexpr (QSPLIT)
+          read_q(32 * w < C::BM / 2 ? XS_OFF : qhi);
+        else
+          read_q(int(Qs - smem));
+      }
     }
     // every wave is done with the LDS region that holds the output (the K/V stages, or in
-    // the persistent form the Q region)
+    // the persistent form the Q region; QSPLIT: Xs and the V stage V_T has left)
     lds_barrier();
-    constexpr int WAVE_LDS = (PERSIST ? C::QB : C::LDS) / WAVES;  // bytes of a wave's region
+    if constexpr (QSPLIT) {
+      // the next tile's K_1, to the K stage the second half of its Q has left
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) dma_kn(Ks + (1 - sbn) * C::TILEB, 1, i);
+    }
+    // bytes of a wave's region (QSPLIT: two waves' regions in each 32 KiB half)
+    constexpr int WAVE_LDS = (PERSIST ? C::QB : C::LDS) / WAVES;
     constexpr int NHALF = (32 * D * 4 + WAVE_LDS - 1) / WAVE_LDS;
+    // QSPLIT: waves 0 .. WAVES/2-1 stage in Xs, the others in the V stage V_T has left
+    const int out_off = !QSPLIT ? int(Qs - smem) + w * WAVE_LDS
+                        : w < WAVES / 2 ? XS_OFF + w * WAVE_LDS
+                                        : 2 * C::TILEB + (1 - sbn) * C::TILEB +
+                                              (w - WAVES / 2) * WAVE_LDS;
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const int row0 = q0 + 32 * (RB * w + r);  // the block's first query row
-      store_rows_lds<D, NHALF>(o[r], mc[r], l[r], LAZY ? lp[r] : l[r], Qs + w * WAVE_LDS,
+      store_rows_lds<D, NHALF>(o[r], mc[r], l[r], LAZY ? lp[r] : l[r], smem + out_off,
                                O + kg * bhn * D + hoff + int64_t(row0) * D,
                                LSE + kg * bhn + int64_t(bh) * N + row0, lane, N - row0);
     }
@@ -765,7 +806,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
 // nsplit key ranges of kps keys each (the last may be shorter, none is empty); with
 // nsplit = 1 and kps = N the kernel writes the attention itself to o and lse
 // STATS: the statistics-recording form, writing to stats (nsplit = 1).
-// With nsplit = 1, at least two key tiles, d = 128 and more tiles than the device holds
+// With nsplit = 1, at least two key tiles, d = 128 or 256 and more tiles than the device holds
 // workgroups at once, the persistent form runs instead: one workgroup per resident slot,
 // each taking its tiles in turn.
 template <int D, bool BF16, int WAVES, int RB, bool STATS = false>
@@ -775,7 +816,7 @@ inline hipError_t run16(const Problem &p, float *o, float *lse, int nsplit, int 
   const int nqt = (p.N + C::BM - 1) / C::BM;
   const int G = nqt * p.B * p.H * nsplit;
   const float c = p.scale * kLog2e;
-  if constexpr (!STATS && D == 128) {
+  if constexpr (!STATS && (D == 128 || D == 256)) {
     if (nsplit == 1 && p.N > C::BN) {
       constexpr auto pk = fa_fwd16_kernel<D, BF16, WAVES, RB, false, true>;
       const int R = resident_workgroups<pk>(C::NT, C::LDSP);

@@ -178,28 +178,31 @@ def test_bitwise_deterministic():
 
 
 # ---- the persistent form --------------------------------------------------------------
-# 16-bit d = 128 problems with more 256-row query tiles than the device holds workgroups at
-# once (256 on MI355X) run as one workgroup per slot taking its tiles in turn, the next
-# tile's Q and first K/V tiles loaded while the current one finishes.  Below: 257 to 900
-# tiles (one to four per workgroup), 2 to 16 key tiles, ragged last key and query tiles.
-@pytest.mark.parametrize("B,H,N,dtype", [(1, 300, 65, "bf16"), (1, 260, 128, "f16"),
-                                        (2, 150, 129, "bf16"), (3, 100, 700, "f16"),
-                                        (1, 257, 256, "bf16"), (2, 75, 1000, "bf16")])
-def test_persistent_form_against_oracle(B, H, N, dtype):
-    m, _, _ = full_case(B, H, N, 128, dtype, seed=700 + N)
-    assert_parity(m, dtype, where=f"persistent {B}x{H}x{N} {dtype}")
+# 16-bit d = 128 and d = 256 problems with more query tiles (256 rows at d = 128, 128 at
+# d = 256) than the device holds workgroups at once (256 on MI355X) run as one workgroup
+# per slot taking its tiles in turn, the next tile's Q and first K/V tiles loaded while the
+# current one finishes.  Below: 257 to 1200 tiles (one to five per workgroup), 2 to 16 key
+# tiles, ragged last key and query tiles.
+@pytest.mark.parametrize("B,H,N,d,dtype", [(1, 300, 65, 128, "bf16"), (1, 260, 128, 128, "f16"),
+                                          (2, 150, 129, 128, "bf16"), (3, 100, 700, 128, "f16"),
+                                          (1, 257, 256, 128, "bf16"), (2, 75, 1000, 128, "bf16"),
+                                          (1, 300, 65, 256, "bf16"), (1, 257, 128, 256, "f16"),
+                                          (2, 100, 700, 256, "bf16"), (3, 30, 1000, 256, "f16")])
+def test_persistent_form_against_oracle(B, H, N, d, dtype):
+    m, _, _ = full_case(B, H, N, d, dtype, seed=700 + N + d)
+    assert_parity(m, dtype, where=f"persistent {B}x{H}x{N}x{d} {dtype}")
 
 
-@pytest.mark.parametrize("H,N,chunk,dtype", [(600, 128, 128, "f16"), (200, 700, 64, "bf16"),
-                                            (96, 2048, 32, "bf16")])
-def test_persistent_form_matches_one_tile_per_workgroup(H, N, chunk, dtype):
+@pytest.mark.parametrize("H,N,d,chunk,dtype", [(600, 128, 128, 128, "f16"), (200, 700, 128, 64, "bf16"),
+                                              (96, 2048, 128, 32, "bf16"), (300, 256, 256, 128, "bf16"),
+                                              (48, 2048, 256, 16, "f16")])
+def test_persistent_form_matches_one_tile_per_workgroup(H, N, d, chunk, dtype):
     # the whole batch (persistent form) against the same heads in calls of at most 256
     # query tiles (one tile per workgroup): the same arithmetic, so bitwise the same
     import torch
 
-    d = 128
-    xd = to_device(make_qkv(1, H, N, d, dtype, seed=900 + N), dtype)
-    say(f"persistent vs per-tile H={H} N={N} {dtype}")
+    xd = to_device(make_qkv(1, H, N, d, dtype, seed=900 + N + d), dtype)
+    say(f"persistent vs per-tile H={H} N={N} d={d} {dtype}")
     o, lse = run("fused", xd, 1.0 / math.sqrt(d))
     for h0 in range(0, H, chunk):
         part = {n: t[:, h0:h0 + chunk] for n, t in xd.items()}

@@ -23,13 +23,17 @@ KNOWN_SCRATCH = {
     r"fa_fwd32_kernelILi256ELb1E": 400,
     r"fa_bwd32_dkdv_kernelILi128E": 84,
 }
-# the persistent forward kernels: scalar spills into vector-register lanes, at most
-PERSISTENT = r"fa_fwd16_kernelILi128ELb[01]ELi8ELi1ELb0ELb1E"
-PERSISTENT_SGPR_SPILLS = 64
+# the persistent forward kernels (d = 128 and 256): scalar spills into vector-register
+# lanes, at most
+PERSISTENT_128 = r"fa_fwd16_kernelILi128ELb[01]ELi8ELi1ELb0ELb1E"
+PERSISTENT_256 = r"fa_fwd16_kernelILi256ELb[01]ELi4ELi1ELb0ELb1E"
+PERSISTENT = f"({PERSISTENT_128}|{PERSISTENT_256})"
+PERSISTENT_SGPR_SPILLS = 96
 # (kernel name pattern, waves per SIMD) of the production 16-bit forward kernels
 OCCUPANCY = [
     (r"fa_fwd16_kernelILi128ELb[01]ELi8ELi1ELb0ELb0E", 2),
-    (PERSISTENT, 2),
+    (PERSISTENT_128, 2),
+    (PERSISTENT_256, 1),
     (r"fa_fwd16_kernelILi64ELb[01]ELi4ELi2ELb0ELb0E", 2),
     (r"fa_fwd16_kernelILi256ELb[01]ELi4ELi1ELb0ELb0E", 1),
 ]
@@ -72,13 +76,16 @@ def test_fast_paths_keep_their_waves_per_simd(usage):
             assert usage[n]["occupancy"] == waves, f"{n}: {usage[n]['occupancy']} waves/SIMD"
 
 
-def test_persistent_kernels_spill_nothing_in_their_steady_loop():
-    # the innermost loop of each persistent kernel (the steady-state key-tile loop) holds
-    # no spill or restore of a scalar register (v_writelane / v_readlane)
+@pytest.mark.parametrize("unit,pattern,mfma", [("fa_fwd16_d128.hip", PERSISTENT_128, 32),
+                                               ("fa_fwd16.hip", PERSISTENT_256, 64)])
+def test_persistent_kernels_spill_nothing_in_their_steady_loop(unit, pattern, mfma):
+    # the innermost loop of each persistent kernel (the steady-state key-tile loop, mfma
+    # products per tile) holds no spill or restore of a scalar register (v_writelane /
+    # v_readlane)
     with tempfile.TemporaryDirectory() as d:
-        asm = build.device_assembly("fa_fwd16_d128.hip", f"{d}/out.s")
+        asm = build.device_assembly(unit, f"{d}/out.s")
     lines = asm.split("\n")
-    starts = [i for i, l in enumerate(lines) if re.match(r"^(_Z\w+):", l) and re.search(PERSISTENT, l)]
+    starts = [i for i, l in enumerate(lines) if re.match(r"^(_Z\w+):", l) and re.search(pattern, l)]
     assert len(starts) == 2, starts
     for st in starts:
         end = next(j for j in range(st, len(lines)) if "s_endpgm" in lines[j])
@@ -91,5 +98,5 @@ def test_persistent_kernels_spill_nothing_in_their_steady_loop():
         back = max(i for i, l in enumerate(body)
                    if ("s_cbranch" in l or "s_branch" in l) and l.split(";")[0].strip().endswith(label))
         loop = [l.split(";")[0].strip() for l in body[lab:back + 1]]
-        assert sum("v_mfma" in l for l in loop) == 32, "not the key-tile loop"
+        assert sum("v_mfma" in l for l in loop) == mfma, "not the key-tile loop"
         assert not [l for l in loop if l.startswith(("v_readlane", "v_writelane"))], body[0]
