@@ -210,6 +210,29 @@ def test_persistent_form_matches_one_tile_per_workgroup(H, N, d, chunk, dtype):
         assert torch.equal(op, o[:, h0:h0 + chunk]) and torch.equal(lp, lse[:, h0:h0 + chunk]), h0
 
 
+def test_persistent_forms_on_concurrent_streams():
+    # two persistent launches (d = 128 and d = 256) and a per-tile one (d = 64) enqueued on
+    # three streams at once, so that their workgroups share the compute units: each result
+    # equals the same call made alone
+    import torch
+
+    import exact_attention_90_amd as fa
+
+    cases = [(1, 300, 256, 128, "bf16"), (1, 300, 128, 256, "f16"), (2, 8, 1024, 64, "bf16")]
+    xs = [to_device(make_qkv(B, H, N, d, dt, seed=60 + i), dt) for i, (B, H, N, d, dt) in enumerate(cases)]
+    say("persistent forms on concurrent streams")
+    alone = [run("fused", x, 1.0 / math.sqrt(c[3])) for x, c in zip(xs, cases)]
+    streams = [torch.cuda.Stream() for _ in cases]
+    outs = []
+    for x, c, st in zip(xs, cases, streams):
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            outs.append(fa.fwd(x["q"], x["k"], x["v"], 1.0 / math.sqrt(c[3])))
+    torch.cuda.synchronize()
+    for (o, lse), (o1, l1) in zip(outs, alone):
+        assert torch.equal(o, o1) and torch.equal(lse, l1)
+
+
 # ---- the named workloads at full size ----------------------------------------------
 def _compare_rows(name, w, o, lse, x, rows):
     """Oracle on `rows` (None: every row) against the kernel's output."""
