@@ -767,9 +767,12 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
     // the persistent form the Q region; QSPLIT: Xs and the V stage V_T has left)
     lds_barrier();
     if constexpr (QSPLIT) {
-      // the next tile's K_1, to the K stage the second half of its Q has left
+      // the next tile's K_1, to the K stage the second half of its Q has left (only if
+      // there is one: nothing may still be loading into LDS when the workgroup ends)
+      if (has_next) {
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) dma_kn(Ks + (1 - sbn) * C::TILEB, 1, i);
+        for (int i = 0; i < CPT; ++i) dma_kn(Ks + (1 - sbn) * C::TILEB, 1, i);
+      }
     }
     // bytes of a wave's region (QSPLIT: two waves' regions in each 32 KiB half)
     constexpr int WAVE_LDS = (PERSIST ? C::QB : C::LDS) / WAVES;
