@@ -88,12 +88,13 @@ struct Cfg16 {
 // tile t each query row's running max (base-2 units, c m) and row sum go to
 // ST[((b H + h) N + i) ceil(N/64) + t][0..1].  The other forms ignore ST.
 //
-// PERSIST: the persistent form (nsplit = 1, at least two key tiles, no STATS).  The grid
-// holds fewer workgroups than the G tiles and workgroup b takes tiles b, b + gridDim.x,
-// b + 2 gridDim.x, ... in turn.  The next tile's Q (into an LDS region of its own) and its
-// first K and V tiles are loaded while the current tile's last key tiles are processed, so
-// that a new tile starts without waiting for memory, and its output goes out through the
-// Q region while the next tile's first K/V tiles sit in the stages.
+// PERSIST: the persistent form (d = 128 or 256, one block per wave, nsplit = 1, at least
+// two key tiles, no STATS).  The grid holds fewer workgroups than the G tiles and
+// workgroup b takes tiles b, b + gridDim.x, b + 2 gridDim.x, ... in turn.  The next tile's
+// Q (d = 128: into an LDS region of its own; d = 256: half there, half into a freed K
+// stage) and its first K and V tiles are loaded while the current tile's last key tiles
+// are processed, so that a new tile starts without waiting for memory, and its output
+// goes out through LDS that the next tile's first K/V tiles do not occupy.
 template <int D, bool BF16, int WAVES, int RB, bool STATS = false, bool PERSIST = false>
 __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd16_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ K,
