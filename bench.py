@@ -101,6 +101,22 @@ def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
+def kernel_form(w, args) -> str:
+    """Which form of the fused 16-bit kernel the library picks for this launch: the
+    persistent one (d = 128 or 256, one key range, at least two key tiles, more query
+    tiles than the device's compute units hold workgroups) or one tile per workgroup."""
+    import torch
+
+    if args.path != "fused" or w.dtype == "f32" or (args.split or 1) != 1:
+        return "one tile per workgroup" if args.path == "fused" else args.path
+    bm = 256 if w.d in (64, 128) else 128
+    tiles = w.B * w.H * -(-w.N // bm)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if w.d in (128, 256) and w.N > 64 and tiles > cus:
+        return f"persistent: {cus // 8 * 8} workgroups, {tiles} query tiles of {bm} rows"
+    return "one tile per workgroup"
+
+
 def committed_traffic(workload: str, path: str):
     """HBM bytes per launch from the committed counter summary, or None when the
     summary is missing or was taken on different kernel source."""
@@ -383,6 +399,7 @@ def main() -> int:
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
             "kernel": "fa_fwd16_kernel" if w.dtype != "f32" else "fa_fwd32_kernel",
+            "form": kernel_form(w, args),
             "avg_launch_ms": round(avg_launch_ms, 5),
             "median_launch_ms": round(statistics.median(per), 5),
             "min_launch_ms": round(min(per), 5),
