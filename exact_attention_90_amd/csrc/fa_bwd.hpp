@@ -30,23 +30,14 @@
 
 namespace fa {
 
-// LDS reads from an absolute 32-bit LDS byte address.  A dynamic-LDS array's own
-// address is a link-time constant that the compiler adds to every offset with a VALU add;
-// folding it into a lane's address once leaves only immediate offsets at the reads.
-typedef __attribute__((address_space(3))) char lds_byte;
+// LDS reads from an absolute 32-bit LDS byte address (lds_addr, lds_read_tr_at in
+// fa_device.hpp)
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-__device__ __forceinline__ uint32_t lds_addr(const char *p) {
-  return uint32_t(uintptr_t((const lds_byte *)p));
-}
 __device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
   return *(const lds_u32x4 *)(uintptr_t)addr;
 }
 __device__ __forceinline__ f32x4 lds_read_f32x4_at(uint32_t addr) {
   return __builtin_bit_cast(f32x4, *(const lds_u32x4 *)(uintptr_t)addr);
-}
-__device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
-  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)addr);
-  return __builtin_bit_cast(u32x2, r);
 }
 
 // A streamed tile is read two ways: 16-byte row reads (the A operand of S = Q K^T and

@@ -187,6 +187,27 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char *l
                  : "memory");
 }
 
+// The same load with its scalar offset soff_base + soff_imm, soff_imm a constant once
+// loops are unrolled: the add runs inside the assembly, in front of the load, where it
+// also stands in the one wait state after the m0 write (SAFE: it and s_nop 3 give 5).
+template <bool SAFE = false>
+__device__ __forceinline__ void buf_load16_lds_off(__amdgpu_buffer_rsrc_t r, char *lds_wave_base,
+                                                   int voff, int soff_base, int soff_imm) {
+  const uint32_t m0v =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)lds_wave_base;
+  int so;
+  if constexpr (SAFE)
+    asm volatile("s_add_i32 %0, %2, %4\n\ts_nop 3\n\tbuffer_load_dwordx4 %1, %3, %0 offen lds"
+                 : "=&s"(so)
+                 : "v"(voff), "s"(soff_base), "s"(r), "i"(soff_imm), "{m0}"(m0v)
+                 : "memory", "scc");
+  else
+    asm volatile("s_add_i32 %0, %2, %4\n\tbuffer_load_dwordx4 %1, %3, %0 offen lds"
+                 : "=&s"(so)
+                 : "v"(voff), "s"(soff_base), "s"(r), "i"(soff_imm), "{m0}"(m0v)
+                 : "memory", "scc");
+}
+
 // Workgroup barrier that orders LDS accesses only: the loads into LDS above are not
 // waited for here (the caller's s_waitcnt vmcnt decides which must have landed).
 __device__ __forceinline__ void lds_barrier() {
@@ -203,6 +224,18 @@ __device__ __forceinline__ void lds_write16(char *base, int byte_off, u32x4 v) {
 }
 __device__ __forceinline__ u32x2 lds_read_tr(const char *base, int byte_off) {
   s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + byte_off));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// LDS reads from an absolute 32-bit LDS byte address.  A dynamic-LDS array's own
+// address is a link-time constant that the compiler adds to every offset with a VALU add;
+// folding it into a lane's address once leaves only immediate offsets at the reads.
+typedef __attribute__((address_space(3))) char lds_byte;
+__device__ __forceinline__ uint32_t lds_addr(const char *p) {
+  return uint32_t(uintptr_t((const lds_byte *)p));
+}
+__device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)addr);
   return __builtin_bit_cast(u32x2, r);
 }
 

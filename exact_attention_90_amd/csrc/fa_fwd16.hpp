@@ -238,12 +238,14 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   auto dma_k = [&](char *kb, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      buf_load16_lds<PERSIST>(krs, kb + dma_wave + i * ST_STEP, st_ki(i), kt * C::TILEB + i * ST_STEP);
+      buf_load16_lds_off<PERSIST>(krs, kb + dma_wave + i * ST_STEP, st_ki(i), kt * C::TILEB,
+                                  i * ST_STEP);
   };
   auto dma_v = [&](char *vb, int kt) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
-      buf_load16_lds<PERSIST>(vrs, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB + i * ST_STEP);
+      buf_load16_lds_off<PERSIST>(vrs, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB,
+                                  i * ST_STEP);
   };
   // one chunk of a tile's load: an iteration's loads ride one per step between its
   // first matrix-core steps instead of all issuing before them (measured: bitwise the
@@ -251,26 +253,28 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // (safe: the form that keeps the scalar operands' wait states, for the steps where the
   // persistent form restores spilled scalars; the steady-state loop has none)
   auto dma_k1 = [&](char *kb, int kt, int i, auto safe) __attribute__((always_inline)) {
-    buf_load16_lds<decltype(safe)::value>(krs, kb + dma_wave + i * ST_STEP, st_ki(i),
-                                          kt * C::TILEB + i * ST_STEP);
+    buf_load16_lds_off<decltype(safe)::value>(krs, kb + dma_wave + i * ST_STEP, st_ki(i),
+                                              kt * C::TILEB, i * ST_STEP);
   };
   auto dma_v1 = [&](char *vb, int kt, int i, auto safe) __attribute__((always_inline)) {
-    buf_load16_lds<decltype(safe)::value>(vrs, vb + dma_wave + i * ST_STEP, st_v,
-                                          kt * C::TILEB + i * ST_STEP);
+    buf_load16_lds_off<decltype(safe)::value>(vrs, vb + dma_wave + i * ST_STEP, st_v,
+                                              kt * C::TILEB, i * ST_STEP);
   };
   // the persistent form's loads of the next tile: chunk i of its K or V tile kt, and
   // chunk i of its Q tile into the Q region (the same swizzled layout as the Q prologue)
   auto dma_kn = [&](char *kb, int kt, int i) __attribute__((always_inline)) {
-    buf_load16_lds<PERSIST>(krn, kb + dma_wave + i * ST_STEP, st_ki(i), kt * C::TILEB + i * ST_STEP);
+    buf_load16_lds_off<PERSIST>(krn, kb + dma_wave + i * ST_STEP, st_ki(i), kt * C::TILEB,
+                                i * ST_STEP);
   };
   auto dma_vn = [&](char *vb, int kt, int i) __attribute__((always_inline)) {
-    buf_load16_lds<PERSIST>(vrn, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB + i * ST_STEP);
+    buf_load16_lds_off<PERSIST>(vrn, vb + dma_wave + i * ST_STEP, st_v, kt * C::TILEB,
+                                i * ST_STEP);
   };
   // chunk i of the next Q tile (rows 8 i .. 8 i + 7 at d = 256) to LDS offset
   // base + i ST_STEP; for QSPLIT the caller passes the base of the chunk's half
   auto dma_qn = [&](int base, int i) __attribute__((always_inline)) {
-    buf_load16_lds<PERSIST>(qrn, smem + (base + i * ST_STEP + dma_wave), st_ki(i),
-                            q0n * C::ROWB + i * ST_STEP);
+    buf_load16_lds_off<PERSIST>(qrn, smem + (base + i * ST_STEP + dma_wave), st_ki(i),
+                                q0n * C::ROWB, i * ST_STEP);
   };
   // bfloat16 V: the P V product runs in binary16, so each thread widens the chunks its
   // own loads wrote (chunk i: 16 bytes at dma_wave + i ST_STEP + 16 lane), in place.
@@ -307,11 +311,23 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
     const int off = kb + ((32 * kc) ^ k_xor) + 32 * t * C::ROWB;
     return lds_read16(smem, off);
   };
-  auto v_op = [&](int vb, int i) __attribute__((always_inline)) {
+  // v_xor is a multiple of 64 below 256, so (64 e) ^ v_xor = 256 (e / 4) + ((64 (e % 4)) ^
+  // v_xor): four absolute lane addresses per V stage (v_bases, once per tile), and every
+  // other part of an operand's address is an immediate of its transposing reads
+  struct VBases {
+    uint32_t c[4];
+  };
+  auto v_bases = [&](int vb) __attribute__((always_inline)) {
+    VBases r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r.c[e] = lds_addr(smem) + uint32_t(vb + ((64 * e) ^ v_xor));
+    return r;
+  };
+  auto v_op = [&](const VBases &vc, int i) __attribute__((always_inline)) {
     const int u = i / OB, e = i % OB;
-    const int off = vb + ((64 * e) ^ v_xor);
-    const u32x2 a0 = lds_read_tr(smem, off + (16 * u) * C::ROWB);
-    const u32x2 a1 = lds_read_tr(smem, off + (16 * u + 8) * C::ROWB);
+    const uint32_t a = vc.c[e % 4] + 256 * (e / 4) + (16 * u) * C::ROWB;
+    const u32x2 a0 = lds_read_tr_at(a);
+    const u32x2 a1 = lds_read_tr_at(a + 8 * C::ROWB);
     return u32x4{a0[0], a0[1], a1[0], a1[1]};
   };
 
@@ -324,11 +340,13 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // units), this lane's partial row sum, and, for the tile whose P is pending, its rescale
   // factor alpha and P row sum; lazy form only: the partial sums of P as rounded to
   // binary16 for the P V product (lp, and rp for the pending tile)
-  float mc[RB], l[RB], alpha[RB], rs[RB], lp[RB], rp[RB];
+  // pq: the newest P value, added to rs one exponential later (the sum keeps score order,
+  // and its add never follows the exponential that produced its operand)
+  float mc[RB], l[RB], alpha[RB], rs[RB], pq[RB], lp[RB], rp[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     mc[r] = -INFINITY;
-    l[r] = alpha[r] = rs[r] = lp[r] = rp[r] = 0.f;
+    l[r] = alpha[r] = rs[r] = pq[r] = lp[r] = rp[r] = 0.f;
   }
   const int nkt = (NK + C::BN - 1) / C::BN;
   const int nlast = NK - (nkt - 1) * C::BN;  // valid keys of the last tile, 1 .. BN
@@ -410,6 +428,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
     sub[r] = (mc_new == -INFINITY) ? 0.f : mc_new;
     mc[r] = mc_new;
     rs[r] = 0.f;
+    pq[r] = 0.f;
     rp[r] = 0.f;
   };
   auto exp_range = [&](int b, int e, int r) __attribute__((always_inline)) {
@@ -418,7 +437,8 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
       if (x >= b && x < e) {
         const float p = ex2(fmaf(s[r][x / 16][x % 16], c, -sub[r]));
         s[r][x / 16][x % 16] = p;
-        rs[r] += p;
+        rs[r] += pq[r];
+        pq[r] = p;
       }
   };
   // keys at or past nvalid of a tile are masked to -inf before its softmax
@@ -484,6 +504,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
     if (k == NEA) {
       pack_u(2, r);
       pack_u(3, r);
+      rs[r] += pq[r];  // the tile's last P value
       l[r] = fmaf(l[r], alpha[r], rs[r]);
       if constexpr (LAZY) lp[r] = fmaf(lp[r], alpha[r], rp[r]);
       if constexpr (STATS) record_stats(r);
@@ -672,8 +693,9 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
         }
 
       // ---- B ----
+      const VBases vc = v_bases(vb);
 #pragma unroll
-      for (int i = 0; i < DV; ++i) vf[i] = v_op(vb, i);
+      for (int i = 0; i < DV; ++i) vf[i] = v_op(vc, i);
       if (MASKED && nlast < C::BN) mask(nlast);
       // bfloat16 V_{j+1} is widened in place during the P V product below, once this
       // wave's loads of it have landed (the loads issued after it may stay in flight)
@@ -689,7 +711,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
           pv_step(i, vf[i % DV], r);
-          if (r == RB - 1 && i + DV < NB) vf[i % DV] = v_op(vb, i + DV);
+          if (r == RB - 1 && i + DV < NB) vf[i % DV] = v_op(vc, i + DV);
           soft_b(i, r);
           {
             // chunk c: read at step (NB / CPT) c + 1, widened and written back at the
@@ -730,7 +752,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
           for (int i = 0; i < CPT; ++i) dma_kn(Ks + (1 - sbn) * C::TILEB, 1, i);
         }
       }
-      const int vb = v_base + (2 + ((nkt - 1 + sb) & 1)) * C::TILEB;
+      const VBases vc = v_bases(v_base + (2 + ((nkt - 1 + sb) & 1)) * C::TILEB);
       st_tile = nkt - 1;
       rescale_lazy();
 #pragma unroll
@@ -740,7 +762,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
       if constexpr (ASMPV) mfma_drain();
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
-        const u32x4 vop = v_op(vb, i);
+        const u32x4 vop = v_op(vc, i);
 #pragma unroll
         for (int r = 0; r < RB; ++r) pv_step(i, vop, r);
       }
@@ -801,7 +823,7 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
 #pragma unroll
       for (int e = 0; e < OB; ++e) o[r][e] = f32x16{};
       mc[r] = -INFINITY;
-      l[r] = alpha[r] = rs[r] = lp[r] = rp[r] = 0.f;
+      l[r] = alpha[r] = rs[r] = pq[r] = lp[r] = rp[r] = 0.f;
     }
   }
 }

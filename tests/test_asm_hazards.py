@@ -220,8 +220,8 @@ def test_the_scan_sees_planted_mistakes():
 
 
 def test_the_scan_sees_a_scalar_written_just_before_a_load_into_lds():
-    # the offset of every load into LDS taken from a v_readfirstlane just before the load,
-    # with the one wait state of the plain form
+    # the offset of every load into LDS of the plain form (the backward kernels' form)
+    # taken from a v_readfirstlane just before the load, with that form's one wait state
     with tempfile.TemporaryDirectory() as d:
         src = os.path.join(d, "csrc")
         shutil.copytree(build.CSRC, src)
@@ -236,7 +236,7 @@ def test_the_scan_sees_a_scalar_written_just_before_a_load_into_lds():
         old = build.CSRC
         build.CSRC = src
         try:
-            asm = build.device_assembly("fa_fwd16.hip", os.path.join(d, "m.s"))
+            asm = build.device_assembly("fa_bwd_d128.hip", os.path.join(d, "m.s"))
         finally:
             build.CSRC = old
         _, bad = _scan(asm)
