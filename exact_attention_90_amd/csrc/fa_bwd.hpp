@@ -30,12 +30,8 @@
 
 namespace fa {
 
-// LDS reads from an absolute 32-bit LDS byte address (lds_addr, lds_read_tr_at in
-// fa_device.hpp)
-typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-__device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
-  return *(const lds_u32x4 *)(uintptr_t)addr;
-}
+// LDS reads from an absolute 32-bit LDS byte address (lds_addr, lds_read16_at and
+// lds_read_tr_at in fa_device.hpp)
 __device__ __forceinline__ f32x4 lds_read_f32x4_at(uint32_t addr) {
   return __builtin_bit_cast(f32x4, *(const lds_u32x4 *)(uintptr_t)addr);
 }

@@ -234,6 +234,10 @@ typedef __attribute__((address_space(3))) char lds_byte;
 __device__ __forceinline__ uint32_t lds_addr(const char *p) {
   return uint32_t(uintptr_t((const lds_byte *)p));
 }
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+__device__ __forceinline__ u32x4 lds_read16_at(uint32_t addr) {
+  return *(const lds_u32x4 *)(uintptr_t)addr;
+}
 __device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
   s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(uintptr_t)addr);
   return __builtin_bit_cast(u32x2, r);
@@ -243,6 +247,24 @@ __device__ __forceinline__ u32x2 lds_read_tr_at(uint32_t addr) {
 // leaves the other counters alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
 // 6:4, lgkmcnt 11:8)
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// the same for LDS operations (lgkmcnt), leaving vmcnt and expcnt alone
+constexpr int lgkmcnt_only(int n) { return 15 | (3 << 14) | (7 << 4) | ((n & 15) << 8); }
+// s_waitcnt lgkmcnt(n) for an n that is a constant once loops are unrolled (the builtin
+// takes only constant expressions; the switch folds away)
+__device__ __forceinline__ void wait_lds(int n) {
+  switch (n) {
+#define FA_WAIT_LDS(k) \
+  case k:              \
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_only(k)); \
+    break;
+    FA_WAIT_LDS(0) FA_WAIT_LDS(1) FA_WAIT_LDS(2) FA_WAIT_LDS(3) FA_WAIT_LDS(4)
+    FA_WAIT_LDS(5) FA_WAIT_LDS(6) FA_WAIT_LDS(7) FA_WAIT_LDS(8) FA_WAIT_LDS(9)
+    FA_WAIT_LDS(10) FA_WAIT_LDS(11) FA_WAIT_LDS(12) FA_WAIT_LDS(13) FA_WAIT_LDS(14)
+#undef FA_WAIT_LDS
+    default:
+      break;
+  }
+}
 
 // ---- schedule pins ----------------------------------------------------------------
 // An empty asm that claims to rewrite x: the value must be computed before this point

@@ -112,6 +112,17 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // d = 64, which must fit two waves per SIMD)
   constexpr int DK = (D == 64 && RB == 2) ? 3 : 4;
   constexpr int DV = (D == 64 && RB == 2) ? 2 : 3;
+  constexpr bool PAIRW = RB == 1;
+  auto imin = [](int a, int b) __attribute__((always_inline)) { return a < b ? a : b; };
+  // LDS accesses of the bfloat16 widening issued in P V steps a .. b-1 (chunk reads on
+  // steps 1 mod NB/CPT, writes on steps -1 mod NB/CPT)
+  auto widen_ops = [](int a, int b) __attribute__((always_inline)) {
+    int n = 0;
+    if constexpr (BF16)
+      for (int k = a < 0 ? 0 : a; k < b; ++k)
+        n += (k % (NB / CPT) == 1) + (k % (NB / CPT) == NB / CPT - 1);
+    return n;
+  };
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char *const Ks = smem;
   char *const Vs = smem + 2 * C::TILEB;
@@ -306,10 +317,22 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // operand of matrix-core step i: S^T step i = (block t = i / KC, k-step i % KC);
   // P V step i = (output block e = i % OB, key step u = i / OB).  kb / vb are the lane's
   // base offsets into the K / V stage being read (stage offset + k_base / v_base).
-  auto k_op = [&](int kb, int i) __attribute__((always_inline)) {
+  // k_xor is a multiple of 32 below 256, so (32 kc) ^ k_xor = 256 (kc / 8) + ((32 (kc % 8))
+  // ^ k_xor): eight absolute lane addresses per K stage (k_bases, once per tile), the rest
+  // of an operand's address an immediate of its read
+  constexpr int NKB = C::KC < 8 ? C::KC : 8;
+  struct KBases {
+    uint32_t c[NKB];
+  };
+  auto k_bases = [&](int kb) __attribute__((always_inline)) {
+    KBases r;
+#pragma unroll
+    for (int e = 0; e < NKB; ++e) r.c[e] = lds_addr(smem) + uint32_t(kb + ((32 * e) ^ k_xor));
+    return r;
+  };
+  auto k_op = [&](const KBases &kcb, int i) __attribute__((always_inline)) {
     const int t = i / C::KC, kc = i % C::KC;  // block-major: all k-steps of block 0 first
-    const int off = kb + ((32 * kc) ^ k_xor) + 32 * t * C::ROWB;
-    return lds_read16(smem, off);
+    return lds_read16_at(kcb.c[kc % 8] + 256 * (kc / 8) + 32 * t * C::ROWB);
   };
   // v_xor is a multiple of 64 below 256, so (64 e) ^ v_xor = 256 (e / 4) + ((64 (e % 4)) ^
   // v_xor): four absolute lane addresses per V stage (v_bases, once per tile), and every
@@ -600,9 +623,10 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   static_assert(!PERSIST || (RB == 1 && (D == 128 || D == 256)),
                 "persistent form: one 32-row block per wave, d = 128 or 256");
   for (;;) {
+    const KBases kc0 = k_bases(k_base + sb * C::TILEB);
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-      const u32x4 kop = k_op(k_base + sb * C::TILEB, i);
+      const u32x4 kop = k_op(kc0, i);
 #pragma unroll
       for (int r = 0; r < RB; ++r) s_step(i, kop, r);
     }
@@ -660,17 +684,26 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
       char *kw = Ks + P * C::TILEB;                       // K_{j+2}
 
       // ---- A ----
+      // (one wait for the operands of two consecutive products, PAIRW: with one query block
+      // per wave each product would otherwise wait for its own; the compiler's waits stay
+      // and find these already met)
       st_tile = j;
       rescale_lazy();
+      const KBases kcb = k_bases(kb);
 #pragma unroll
-      for (int i = 0; i < DK; ++i) kf[i] = k_op(kb, i);
+      for (int i = 0; i < DK; ++i) kf[i] = k_op(kcb, i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NA; ++i)
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
+          // K reads of steps i + 2 .. min(i + DK, NA) - 1 may stay in flight
+          if (PAIRW && r == 0 && i % 2 == 0 && i + 1 < NA) {
+            wait_lds(imin(DK - 2, NA - i - 2));
+            __builtin_amdgcn_sched_barrier(0);  // the products stay behind the wait
+          }
           s_step(i, kf[i % DK], r);
-          if (r == RB - 1 && i + DK < NA) kf[i % DK] = k_op(kb, i + DK);
+          if (r == RB - 1 && i + DK < NA) kf[i % DK] = k_op(kcb, i + DK);
           // V_{j+1} first (B waits for it alone), then K_{j+2}
           if (r == 0 && i < CPT) dma_v1(vw, j + 1, i, std::integral_constant<bool, NEXT>{});
           if (r == 0 && i >= CPT && i < 2 * CPT) {
@@ -710,6 +743,12 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
       for (int i = 0; i < NB; ++i)
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
+          // V reads of steps i + 2 .. min(i + DV, NB) - 1 (two each) and the widening's LDS
+          // accesses of the steps since then may stay in flight
+          if (PAIRW && r == 0 && i % 2 == 0 && i + 1 < NB) {
+            wait_lds(2 * imin(DV - 2, NB - i - 2) + widen_ops(i + 2 - DV, i));
+            __builtin_amdgcn_sched_barrier(0);
+          }
           pv_step(i, vf[i % DV], r);
           if (r == RB - 1 && i + DV < NB) vf[i % DV] = v_op(vc, i + DV);
           soft_b(i, r);
