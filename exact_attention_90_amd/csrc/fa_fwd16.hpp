@@ -625,10 +625,13 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   for (;;) {
     const KBases kc0 = k_bases(k_base + sb * C::TILEB);
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const u32x4 kop = k_op(kc0, i);
+    for (int i = 0; i < DK; ++i) kf[i] = k_op(kc0, i);
 #pragma unroll
-      for (int r = 0; r < RB; ++r) s_step(i, kop, r);
+    for (int i = 0; i < NA; ++i) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) s_step(i, kf[i % DK], r);
+      if (i + DK < NA) kf[i % DK] = k_op(kc0, i + DK);
+      __builtin_amdgcn_sched_barrier(0);  // the reads stay DK steps ahead of their products
     }
     if (nkt == 1 && nlast < C::BN) mask(nlast);
     if constexpr (EARLY_MAX) {
