@@ -79,7 +79,7 @@ __device__ __forceinline__ void pair_values(float x, float &lo, float &hi) {
 __device__ __forceinline__ float pair_max(float x) {
   float a, b;
   pair_values(x, a, b);
-  return fmaxf(a, b);
+  return __builtin_elementwise_maximum(a, b);  // (finite or -inf operands: as fmaxf)
 }
 __device__ __forceinline__ float pair_sum(float x) {
   float a, b;

@@ -425,11 +425,13 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
   // per SIMD.)
   constexpr bool ASMPV = (RB == 2 && D > 64) || D == 256;
   constexpr int NAM = KC - 2;  // A steps carrying the key-block-0 max
+  // the row max takes IEEE maximum, not fmaxf: the scores are finite or -inf, where the two
+  // agree, and maximum needs no quieting of its operands (three-input v_maximum3_f32)
   auto max_range = [&](int b, int e, int r) __attribute__((always_inline)) {
     if (b == 0) mx[r] = s[r][0][0];
 #pragma unroll
     for (int x = 0; x < 32; ++x)
-      if (x >= b && x < e) mx[r] = fmaxf(mx[r], s[r][x / 16][x % 16]);
+      if (x >= b && x < e) mx[r] = __builtin_elementwise_maximum(mx[r], s[r][x / 16][x % 16]);
   };
   auto max_a = [&](int k, int r) __attribute__((always_inline)) {  // A step KC + 2 + k
     max_range(k * 16 / NAM, (k + 1) * 16 / NAM, r);
@@ -445,7 +447,8 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
     // running max in base-2 units (lazy: the reference, moved only past mc + kTau;
     // -inf + kTau stays -inf, so the first tile with a valid key always sets it)
     const float mxc = m * c;
-    const float mc_new = LAZY ? (mxc > mc[r] + kTau ? mxc : mc[r]) : fmaxf(mc[r], mxc);
+    const float mc_new = LAZY ? (mxc > mc[r] + kTau ? mxc : mc[r])
+                               : __builtin_elementwise_maximum(mc[r], mxc);
     // a row that has seen only masked keys keeps alpha = 0 and P = 0 (no inf - inf)
     alpha[r] = (mc[r] == -INFINITY) ? 0.f : ex2(mc[r] - mc_new);
     sub[r] = (mc_new == -INFINITY) ? 0.f : mc_new;
