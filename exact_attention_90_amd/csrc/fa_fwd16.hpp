@@ -676,6 +676,9 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
       constexpr bool MASKED = decltype(masked)::value;
       constexpr bool NEXT = PERSIST && MASKED;
       constexpr int QSTEPS = NA - 2 * CPT;  // A steps that carry the next tile's Q
+      // first A step of K_{j+2}'s loads: at d = 256 (one wave per SIMD) in the second half
+      // of A, whose steps carry no softmax work, instead of right after V_{j+1}'s
+      constexpr int K0 = (D == 256 && !NEXT) ? NA / 2 : CPT;
       // chunks of the next Q issued here (QSPLIT: the half bound for Xs)
       constexpr int QIN = QSPLIT ? C::QCPT / 2 : C::QCPT;
       static_assert(!NEXT || QSTEPS >= 1, "the next tile's Q needs A steps of its own");
@@ -712,11 +715,11 @@ __global__ __launch_bounds__(64 * WAVES, (Cfg16<D, WAVES, RB>::WPE)) void fa_fwd
           if (r == RB - 1 && i + DK < NA) kf[i % DK] = k_op(kcb, i + DK);
           // V_{j+1} first (B waits for it alone), then K_{j+2}
           if (r == 0 && i < CPT) dma_v1(vw, j + 1, i, std::integral_constant<bool, NEXT>{});
-          if (r == 0 && i >= CPT && i < 2 * CPT) {
+          if (r == 0 && i >= K0 && i < K0 + CPT) {
             if constexpr (NEXT)
-              dma_kn(kw, 0, i - CPT);
+              dma_kn(kw, 0, i - K0);
             else
-              dma_k1(kw, j + 2, i - CPT, std::false_type{});
+              dma_k1(kw, j + 2, i - K0, std::false_type{});
           }
           if constexpr (NEXT) {
 #pragma unroll
